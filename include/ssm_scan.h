@@ -1,0 +1,172 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ * (libssmscan.so).
+ *
+ * The operation is the Mamba selective-scan forward pass as the pages below
+ * define it, plus the bare scan of affine pairs it is built on.
+ *
+ * Pages cited:
+ *   [Scan page]    "Hardware-aware parallel associative scan for Mamba"
+ *                  (http://www.pwwt.cn/news/6375169/)
+ *   [Mamba-2 page] "Mamba (part 2): parallel scan and hardware-aware
+ *                  optimisation" (https://scwacadex.pages.dev/posts/blog8_mamba_parallel_scan/)
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *   row-major in the layouts stated per argument.  The library never frees
+ *   or keeps them.  Pointers must be 16-byte aligned.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *   on it and the call returns without waiting; results are ready when the
+ *   stream is.  Faults inside a kernel therefore surface at the caller's
+ *   next synchronisation of that stream.
+ * - Every argument is validated on the host before any HIP call is made, so
+ *   a bad argument never reaches the GPU.
+ * - Return value: one of the SSM_* status codes below.  On failure a
+ *   description is available from ssm_last_error() on the same thread.
+ * - Outputs must not overlap inputs unless an entry point says otherwise.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SSM_OK           0  /* enqueued successfully */
+#define SSM_EINVAL       1  /* null required pointer, size <= 0, misaligned
+                               pointer, overlapping output, bad flag value */
+#define SSM_EUNSUPPORTED 2  /* valid request this build does not implement
+                               (dtype, d_state > 16, too many chunks) */
+#define SSM_EHIP         3  /* the HIP runtime reported an error */
+#define SSM_ENOMEM       4  /* the two-pass workspace could not be allocated */
+
+/* Storage type of u, delta, B, C, z and y.  A, D, delta_bias and
+ * last_state are always float32; all arithmetic is float32. */
+#define SSM_F32  0
+#define SSM_BF16 1
+
+/* Plans of ssm_scan_fwd_plan. */
+#define SSM_PLAN_AUTO    0  /* what ssm_scan_fwd uses (see ssm_scan_plan_for) */
+#define SSM_PLAN_CARRY   1  /* one launch; each workgroup carries the state
+                               over the whole length L */
+#define SSM_PLAN_TWOPASS 2  /* chunk aggregates -> scan over chunks -> fix-up */
+
+/*
+ * ssm_scan_fwd -- selective-scan forward pass ([Scan page] §1.1-§1.2,
+ * §2.3; [Mamba-2 page] §2.1 and §4.1).
+ *
+ * For every batch row b < batch, channel d < d_inner and step t < L, with
+ * the state h[b,d,:] starting at zero:
+ *     x     = delta[b,d,t] + delta_bias[d]          (delta_bias NULL -> 0)
+ *     Delta = softplus(x) if delta_softplus else x
+ *     a_n   = exp(Delta * A[d,n])
+ *     h_n   = a_n * h_n + Delta * B[b,n,t] * u[b,d,t]
+ *     y     = sum_n C[b,n,t] * h_n + D[d] * u[b,d,t] (D NULL -> 0)
+ *     y    *= silu(z[b,d,t])                         (z NULL -> no gate)
+ *     y[b,d,t] = y  (rounded to nearest even when stored as bfloat16)
+ * and last_state[b,d,n] = h_n after step L-1.
+ *
+ * Arguments (all device pointers):
+ *   u, delta, z : [batch, d_inner, L], dtype `dtype`, L contiguous.
+ *   A           : [d_inner, d_state] float32 (the diagonal state matrix;
+ *                 negative values give decays in (0, 1)).
+ *   B, C        : [batch, d_state, L], dtype `dtype`, shared by all channels.
+ *   D, delta_bias : [d_inner] float32, nullable.
+ *   delta_softplus : 0 or 1.
+ *   y           : [batch, d_inner, L], dtype `dtype`, output; must not
+ *                 overlap any input.
+ *   last_state  : [batch, d_inner, d_state] float32 output, nullable.
+ *   batch, d_inner, d_state, L : sizes, all > 0; d_state <= 16.
+ *   dtype       : SSM_F32 or SSM_BF16.
+ *   stream      : hipStream_t.
+ * Errors: SSM_EINVAL (bad pointer/size/flag), SSM_EUNSUPPORTED (dtype,
+ * d_state > 16), SSM_EHIP, SSM_ENOMEM (two-pass workspace).
+ * The two-pass plan allocates its workspace with hipMallocAsync on `stream`
+ * and frees it with hipFreeAsync on the same stream.
+ */
+int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 void *y, float *last_state,
+                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                 int dtype, void *stream);
+
+/*
+ * ssm_scan_fwd_plan -- ssm_scan_fwd with an explicit plan
+ * ([Scan page] §2.2 and §3.3 describe both decompositions).
+ *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY or SSM_PLAN_TWOPASS.
+ *   states_per_wave : how many of the d_state states one wavefront carries
+ *                     per channel (2, 4 or 8; 0 = automatic).
+ *   chunk           : two-pass chunk length in steps, a multiple of 64
+ *                     (0 = automatic; ignored by the carry plan).
+ * Same semantics, arguments and errors as ssm_scan_fwd otherwise; results of
+ * the plans agree to float32 rounding, not bit for bit.
+ */
+int ssm_scan_fwd_plan(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                      void *y, float *last_state,
+                      int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                      int dtype, int plan, int states_per_wave, int64_t chunk, void *stream);
+
+/*
+ * ssm_scan_plan_for -- the plan, states per wave and chunk length that
+ * SSM_PLAN_AUTO picks for a problem size (host only, no HIP call).
+ * Any output pointer may be NULL.  Returns SSM_OK or SSM_EINVAL.
+ */
+int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
+                      int *plan, int *states_per_wave, int64_t *chunk);
+
+/*
+ * affine_scan -- inclusive scan of affine pairs along each row
+ * ([Scan page] §1.2 and §2.1; [Mamba-2 page] §2.2).
+ * A pair (a, b) is the map h -> a*h + b; composition, later step first, is
+ *     (a2, b2) o (a1, b1) = (a2*a1, a2*b1 + b2),  identity (1, 0).
+ * For each row r and step t:
+ *     out_a[r,t] = a[r,t] * out_a[r,t-1],   out_b[r,t] = a[r,t]*out_b[r,t-1] + b[r,t]
+ * starting from (1, 0), i.e. out_b is h_t with h_0 = 0.
+ *   a, b         : [rows, L] float32 inputs.
+ *   out_a        : [rows, L] float32 output, nullable (products not written).
+ *   out_b        : [rows, L] float32 output.
+ *   Each output may equal its own input (in place) or be disjoint from all
+ *   inputs; partial overlap is SSM_EINVAL.
+ * Rounding: float32 with a fused multiply-add for a*b + c, evaluated in the
+ * fixed association order that affine_scan_order() describes, so results are
+ * reproducible bit for bit from run to run and by any replay of that order.
+ * That order, with T = items per lane, 64 lanes per wave, W waves per block
+ * and chunk = 64*W*T:
+ *   chunks of each row are taken in order with a carry starting at (1, 0);
+ *   item j of lane l of wave w of chunk k is step k*chunk + (w*64 + l)*T + j,
+ *   steps past L being identities.  (1) each lane folds its T items left to
+ *   right from its first item; (2) the lane totals are scanned inside each
+ *   wave in rounds d = 1, 2, 4, 8 (lane l takes lane l-d if l mod 16 >= d),
+ *   then 16 (lanes with bit 4 set take lane 16*floor(l/16)-1) and 32 (lanes
+ *   >= 32 take lane 31), every lane composing own o taken with the identity
+ *   where it takes nothing; (3) lane l's exclusive prefix is lane l-1's
+ *   inclusive value; (4) acc = carry folded with the totals of waves
+ *   0..w-1 in order; a lane starts from (exclusive o acc), lane 0 from acc;
+ *   the next carry folds all W totals; (5) each lane re-folds its items from
+ *   its start, writing every prefix.
+ */
+int affine_scan(const float *a, const float *b, float *out_a, float *out_b,
+                int64_t rows, int64_t L, void *stream);
+
+/*
+ * affine_scan_order -- the constants of affine_scan's association order
+ * (host only).  Any pointer may be NULL.  Returns SSM_OK.
+ */
+int affine_scan_order(int *items_per_lane, int *lanes, int *waves, int *chunk);
+
+/*
+ * ssm_last_error -- text of the last failure on the calling thread
+ * ("" if none).  The pointer stays valid until that thread's next call.
+ */
+const char *ssm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

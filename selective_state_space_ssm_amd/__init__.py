@@ -1,0 +1,198 @@
+"""MI355X (gfx950) selective-scan forward: thin Python binding of libssmscan.so.
+
+Every function here only checks and marshals arguments (torch tensors ->
+device pointers, the current HIP stream) and calls the C ABI declared in
+``include/ssm_scan.h``; all arithmetic runs in the HIP kernels.  There is no
+CPU fallback: if the library is missing or no GPU is present the calls raise.
+
+    y, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus=True)
+    out_a, out_b  = affine_scan(a, b)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["SSMError", "ssm_scan_fwd", "affine_scan", "affine_scan_order", "plan_for",
+           "library_path", "load_library", "PLANS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+_lib = None
+
+SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EHIP, SSM_ENOMEM = 0, 1, 2, 3, 4
+SSM_F32, SSM_BF16 = 0, 1
+PLANS = {"auto": 0, "carry": 1, "twopass": 2}
+_PLAN_NAMES = {v: k for k, v in PLANS.items()}
+_STATUS = {SSM_EINVAL: "invalid argument", SSM_EUNSUPPORTED: "unsupported", SSM_EHIP: "HIP error",
+           SSM_ENOMEM: "out of memory"}
+
+
+class SSMError(RuntimeError):
+    """A non-zero status from the C ABI; ``code`` is the SSM_* value."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, 'error')} ({code}): {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libssmscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(the selective scan has no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
+    lib.ssm_scan_fwd.restype = I
+    lib.ssm_scan_fwd_plan.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, I, I, I64, P]
+    lib.ssm_scan_fwd_plan.restype = I
+    lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
+                                      ctypes.POINTER(I64)]
+    lib.ssm_scan_plan_for.restype = I
+    lib.affine_scan.argtypes = [P, P, P, P, I64, I64, P]
+    lib.affine_scan.restype = I
+    lib.affine_scan_order.argtypes = [ctypes.POINTER(I)] * 4
+    lib.affine_scan_order.restype = I
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SSM_OK:
+        msg = load_library().ssm_last_error().decode(errors="replace")
+        raise SSMError(rc, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, device, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                 return_last_state: bool = True, plan: str = "auto", states_per_wave: int = 0,
+                 chunk: int = 0, y: Optional[torch.Tensor] = None,
+                 last_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective-scan forward on the GPU (see ``ssm_scan_fwd`` in include/ssm_scan.h).
+
+    u, delta, z: [b, d, L]; B, C: [b, n, L] -- all float32 or all bfloat16.
+    A: [d, n] float32; D, delta_bias: [d] float32 or None.
+    Returns (y [b, d, L] in the input dtype, last_state [b, d, n] float32 or None).
+    """
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_fwd needs CUDA/HIP tensors")
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [b, d, L] and A [d, n]")
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    dt = u.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    _need(u, "u", dt, device, (bsz, dim, L))
+    _need(delta, "delta", dt, device, (bsz, dim, L))
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(B, "B", dt, device, (bsz, n, L))
+    _need(C, "C", dt, device, (bsz, n, L))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    if D is not None:
+        _need(D, "D", torch.float32, device, (dim,))
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", torch.float32, device, (dim,))
+    if plan not in PLANS:
+        raise ValueError(f"plan must be one of {list(PLANS)}")
+    if y is None:
+        y = torch.empty_like(u)
+    else:
+        _need(y, "y", dt, device, (bsz, dim, L))
+    if return_last_state and last_state is None:
+        last_state = torch.empty((bsz, dim, n), device=device, dtype=torch.float32)
+    elif last_state is not None:
+        _need(last_state, "last_state", torch.float32, device, (bsz, dim, n))
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_fwd_plan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+                                   bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16,
+                                   PLANS[plan], int(states_per_wave), int(chunk), _stream(device))
+    _check(rc)
+    return y, last_state
+
+
+def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,
+                out_a: Optional[torch.Tensor] = None,
+                out_b: Optional[torch.Tensor] = None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """Inclusive scan of affine pairs along the last axis of [rows, L] float32
+    tensors (see ``affine_scan`` in include/ssm_scan.h).  Returns (out_a or
+    None, out_b).  out_a / out_b may be given, including a / b themselves."""
+    device = a.device
+    if device.type != "cuda":
+        raise ValueError("affine_scan needs CUDA/HIP tensors")
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, L]")
+    rows, L = a.shape
+    _need(a, "a", torch.float32, device, (rows, L))
+    _need(b, "b", torch.float32, device, (rows, L))
+    if out_b is None:
+        out_b = torch.empty_like(b)
+    else:
+        _need(out_b, "out_b", torch.float32, device, (rows, L))
+    if return_a and out_a is None:
+        out_a = torch.empty_like(a)
+    elif out_a is not None:
+        _need(out_a, "out_a", torch.float32, device, (rows, L))
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.affine_scan(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), rows, L, _stream(device))
+    _check(rc)
+    return out_a, out_b
+
+
+def affine_scan_order() -> dict:
+    """Constants of affine_scan's association order (host only)."""
+    lib = load_library()
+    vals = [ctypes.c_int() for _ in range(4)]
+    _check(lib.affine_scan_order(*[ctypes.byref(v) for v in vals]))
+    return dict(zip(("items_per_lane", "lanes", "waves", "chunk"), (v.value for v in vals)))
+
+
+def plan_for(batch: int, d_inner: int, d_state: int, L: int, dtype=torch.float32) -> dict:
+    """The plan the library's automatic choice takes for a size (host only)."""
+    lib = load_library()
+    pl, s = ctypes.c_int(), ctypes.c_int()
+    ch = ctypes.c_int64()
+    code = SSM_F32 if dtype in (torch.float32, "f32") else SSM_BF16
+    _check(lib.ssm_scan_plan_for(batch, d_inner, d_state, L, code, ctypes.byref(pl), ctypes.byref(s),
+                                 ctypes.byref(ch)))
+    return {"plan": _PLAN_NAMES[pl.value], "states_per_wave": s.value, "chunk": ch.value}

@@ -1,0 +1,277 @@
+// Host side of the C ABI declared in include/ssm_scan.h: argument checks
+// (all before any HIP call), plan selection, two-pass workspace, launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "ssm_kernels.h"
+#include "ssm_scan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SSM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [p, p + n) of a possibly-null pointer.
+struct Range {
+  uintptr_t lo, hi;
+  bool valid;
+};
+Range range_of(const void* p, uint64_t bytes) {
+  Range r;
+  r.valid = p != nullptr && bytes > 0;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + bytes;
+  return r;
+}
+bool overlap(const Range& a, const Range& b) { return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi; }
+
+// x*y with an overflow check against 2^62.
+bool mul_ok(int64_t x, int64_t y, int64_t* out) {
+  const int64_t lim = int64_t(1) << 62;
+  if (x < 0 || y < 0) return false;
+  if (x != 0 && y > lim / x) return false;
+  *out = x * y;
+  return true;
+}
+
+constexpr int kSimds = 256 * 4;    // MI355X: 256 CUs x 4 SIMDs
+constexpr int64_t kMaxChunks = 65535;
+constexpr int64_t kMinChunk = 1024;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Waves per state group count G for S states per wave (G is rounded up to a
+// power of two that the kernels are instantiated for).
+int groups_for(int64_t dstate, int S) {
+  int64_t g = ceil_div(dstate, S);
+  int G = 1;
+  while (G < g) G *= 2;
+  return G;
+}
+
+bool sg_instantiated(int S, int G) {
+  switch (S) {
+    case 2: return G == 1 || G == 2 || G == 4 || G == 8;
+    case 4: return G == 1 || G == 2 || G == 4;
+    case 8: return G == 1 || G == 2;
+    default: return false;
+  }
+}
+
+// Plan choice.  The carry plan keeps one state vector per (channel, state
+// group) in registers for the whole length; it fills the GPU when there are
+// at least ~2 wavefronts per SIMD.  With too few channels for that, the
+// two-pass plan splits L into K chunks ([Scan page] §2.2: chunk aggregates,
+// a scan over the K chunk totals, then the fix-up) to multiply the number of
+// wavefronts by K.
+void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
+  const int64_t blocks = batch * ceil_div(dim, 64);
+  int S = 2;
+  for (int cand : {8, 4}) {
+    const int G = groups_for(dstate, cand);
+    if (!sg_instantiated(cand, G)) continue;
+    if (blocks * G >= 2 * kSimds) {
+      S = cand;
+      break;
+    }
+  }
+  const int64_t waves = blocks * groups_for(dstate, S);
+  int64_t chunk = L;
+  int pl = SSM_PLAN_CARRY;
+  if (waves < kSimds && L >= 2 * kMinChunk) {
+    int64_t K = ceil_div(2 * kSimds, waves);
+    if (K > L / kMinChunk) K = L / kMinChunk;
+    if (K > kMaxChunks) K = kMaxChunks;
+    if (K >= 2) {
+      chunk = ceil_div(ceil_div(L, K), 64) * 64;
+      pl = SSM_PLAN_TWOPASS;
+    }
+  }
+  if (plan) *plan = pl;
+  if (S_out) *S_out = S;
+  if (chunk_out) *chunk_out = chunk;
+}
+
+int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t L) {
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || L <= 0)
+    return fail(SSM_EINVAL, "sizes must be positive (batch=%lld d_inner=%lld d_state=%lld L=%lld)",
+                (long long)batch, (long long)dim, (long long)dstate, (long long)L);
+  if (dstate > 16) return fail(SSM_EUNSUPPORTED, "d_state=%lld > 16 is not supported", (long long)dstate);
+  if (batch > 65535) return fail(SSM_EUNSUPPORTED, "batch=%lld > 65535 is not supported", (long long)batch);
+  int64_t bd, bdl, bnl;
+  if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, L, &bdl) || !mul_ok(batch * dstate, L, &bnl) || bdl > (int64_t(1) << 60))
+    return fail(SSM_EINVAL, "tensor sizes overflow");
+  return SSM_OK;
+}
+
+int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int delta_softplus, void* y, float* last_state,
+                  int64_t batch, int64_t dim, int64_t dstate, int64_t L, int dtype, int plan, int S_req,
+                  int64_t chunk_req, void* stream) {
+  g_err.clear();
+  if (!u || !delta || !A || !B || !C || !y)
+    return fail(SSM_EINVAL, "u, delta, A, B, C and y must not be NULL");
+  if (int rc = check_sizes(batch, dim, dstate, L)) return rc;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
+  if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS)
+    return fail(SSM_EINVAL, "unknown plan %d", plan);
+  if (S_req != 0 && S_req != 2 && S_req != 4 && S_req != 8)
+    return fail(SSM_EINVAL, "states_per_wave must be 0, 2, 4 or 8 (got %d)", S_req);
+  if (chunk_req < 0 || chunk_req % 64 != 0) return fail(SSM_EINVAL, "chunk must be 0 or a positive multiple of 64");
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, last_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+
+  const uint64_t es = dtype == SSM_F32 ? 4 : 2;
+  const uint64_t nbdl = uint64_t(batch) * dim * L, nbnl = uint64_t(batch) * dstate * L;
+  const Range rin[] = {range_of(u, nbdl * es), range_of(delta, nbdl * es), range_of(z, nbdl * es),
+                       range_of(B, nbnl * es), range_of(C, nbnl * es), range_of(A, uint64_t(dim) * dstate * 4),
+                       range_of(D, uint64_t(dim) * 4), range_of(delta_bias, uint64_t(dim) * 4)};
+  const Range ry = range_of(y, nbdl * es);
+  const Range rl = range_of(last_state, uint64_t(batch) * dim * dstate * 4);
+  for (const Range& r : rin)
+    if (overlap(ry, r) || overlap(rl, r)) return fail(SSM_EINVAL, "outputs must not overlap inputs");
+  if (overlap(ry, rl)) return fail(SSM_EINVAL, "y and last_state overlap");
+
+  int pl, S;
+  int64_t chunk;
+  choose(batch, dim, dstate, L, &pl, &S, &chunk);
+  if (plan != SSM_PLAN_AUTO) pl = plan;
+  if (S_req) S = S_req;
+  if (S > 2 && !sg_instantiated(S, groups_for(dstate, S))) S = 2;
+  const int G = groups_for(dstate, S);
+  if (!sg_instantiated(S, G)) return fail(SSM_EUNSUPPORTED, "no kernel for %d states per wave x %d waves", S, G);
+  if (pl == SSM_PLAN_TWOPASS) {
+    if (chunk_req)
+      chunk = chunk_req;
+    else if (chunk >= L)  // two-pass forced where auto would not split: two chunks
+      chunk = ceil_div(ceil_div(L, 2), 64) * 64;
+    if (chunk >= L) pl = SSM_PLAN_CARRY;  // a single chunk is the carry plan
+  }
+
+  ssm::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.y = y; a.last_state = last_state; a.h_init = nullptr; a.agg_p = nullptr; a.agg_h = nullptr;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.L = L; a.softplus = delta_softplus;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SSM_BF16;
+
+  if (pl == SSM_PLAN_CARRY) {
+    a.chunk = L;
+    hipError_t e = ssm::launch_cs_full(a, bf16, S, G, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
+    return SSM_OK;
+  }
+
+  const int64_t K = ceil_div(L, chunk);
+  if (K > kMaxChunks) return fail(SSM_EUNSUPPORTED, "%lld chunks exceed the limit of %lld", (long long)K,
+                                  (long long)kMaxChunks);
+  const int64_t rows = batch * dstate * dim;
+  const size_t per = sizeof(float) * static_cast<size_t>(rows) * static_cast<size_t>(K);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, 3 * per, st);
+  if (e == hipErrorOutOfMemory) return fail(SSM_ENOMEM, "two-pass workspace of %zu bytes", 3 * per);
+  if (e != hipSuccess) return hip_fail(e, "two-pass workspace allocation");
+  float* agg_p = static_cast<float*>(ws);
+  float* agg_h = agg_p + rows * K;
+  float* h_init = agg_h + rows * K;
+  a.chunk = chunk;
+  a.agg_p = agg_p;
+  a.agg_h = agg_h;
+  e = ssm::launch_cs_agg(a, bf16, S, G, K - 1, st);
+  if (e == hipSuccess) e = ssm::launch_combine(agg_p, agg_h, h_init, rows, K, st);
+  if (e == hipSuccess) {
+    a.agg_p = nullptr;
+    a.agg_h = nullptr;
+    a.h_init = h_init;
+    e = ssm::launch_cs_full(a, bf16, S, G, K, st);
+  }
+  hipError_t ef = hipFreeAsync(ws, st);
+  if (e != hipSuccess) return hip_fail(e, "two-pass launch");
+  if (ef != hipSuccess) return hip_fail(ef, "two-pass workspace release");
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int delta_softplus, void* y, float* last_state,
+                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, last_state, batch, d_inner, d_state,
+                       L, dtype, SSM_PLAN_AUTO, 0, 0, stream);
+}
+
+int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                      float* last_state, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
+                      int plan, int states_per_wave, int64_t chunk, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, last_state, batch, d_inner, d_state,
+                       L, dtype, plan, states_per_wave, chunk, stream);
+}
+
+int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int* plan,
+                      int* states_per_wave, int64_t* chunk) {
+  g_err.clear();
+  if (int rc = check_sizes(batch, d_inner, d_state, L)) return rc;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  choose(batch, d_inner, d_state, L, plan, states_per_wave, chunk);
+  return SSM_OK;
+}
+
+int affine_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t rows, int64_t L,
+                void* stream) {
+  g_err.clear();
+  if (!a || !b || !out_b) return fail(SSM_EINVAL, "a, b and out_b must not be NULL");
+  if (rows <= 0 || L <= 0) return fail(SSM_EINVAL, "rows and L must be positive");
+  int64_t n;
+  if (!mul_ok(rows, L, &n) || n > (int64_t(1) << 60)) return fail(SSM_EINVAL, "tensor sizes overflow");
+  const void* ptrs[] = {a, b, out_a, out_b};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const uint64_t bytes = uint64_t(n) * 4;
+  const Range ra = range_of(a, bytes), rb = range_of(b, bytes), roa = range_of(out_a, bytes),
+              rob = range_of(out_b, bytes);
+  if (overlap(roa, rob)) return fail(SSM_EINVAL, "out_a and out_b overlap");
+  if (!(out_b == b) && (overlap(rob, ra) || overlap(rob, rb)))
+    return fail(SSM_EINVAL, "out_b must equal b or be disjoint from the inputs");
+  if (out_a && !(out_a == a) && (overlap(roa, ra) || overlap(roa, rb)))
+    return fail(SSM_EINVAL, "out_a must equal a or be disjoint from the inputs");
+  if (out_b == b && overlap(rob, ra)) return fail(SSM_EINVAL, "a and b overlap");
+  hipError_t e = ssm::launch_affine_scan(a, b, out_a, out_b, rows, L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "affine_scan launch");
+  return SSM_OK;
+}
+
+int affine_scan_order(int* items_per_lane, int* lanes, int* waves, int* chunk) {
+  if (items_per_lane) *items_per_lane = ssm::kAffT;
+  if (lanes) *lanes = ssm::kAffLanes;
+  if (waves) *waves = ssm::kAffW;
+  if (chunk) *chunk = ssm::kAffChunk;
+  return SSM_OK;
+}
+
+const char* ssm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

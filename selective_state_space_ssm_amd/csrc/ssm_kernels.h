@@ -1,0 +1,53 @@
+// Internal interface between the host C ABI (capi.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+enum { kFull = 0, kAgg = 1 };
+
+// Arguments of the channel-serial selective-scan kernel (by value).
+struct FwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // nullable
+  const void* z;            // nullable: no gate
+  const float* bias;        // nullable
+  void* y;                  // kFull
+  float* last_state;        // kFull, nullable
+  const float* h_init;      // kFull: [K][b][n][d] chunk start states, nullable (zero)
+  float* agg_p;             // kAgg: [K][b][n][d] chunk decay products
+  float* agg_h;             // kAgg: [K][b][n][d] chunk end states from zero
+  int64_t batch, dim, dstate, L;
+  int64_t chunk;            // steps per chunk (grid z); = L for one chunk
+  int softplus;
+};
+
+// Sizes and flags of one channel-serial launch (by value).
+struct CsSizes {
+  int64_t batch, dim, dstate, L;
+  int64_t chunk;
+  int softplus;
+};
+
+size_t cs_smem_bytes(int G, int mode);
+int cs_time_tile();
+hipError_t launch_cs_full(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);
+hipError_t launch_cs_agg(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);
+hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,
+                          hipStream_t st);
+
+// affine_scan association-order constants and launcher
+constexpr int kAffT = 8;      // items per lane
+constexpr int kAffLanes = 64; // lanes per wave
+constexpr int kAffW = 4;      // waves per block
+constexpr int kAffChunk = kAffT * kAffLanes * kAffW;
+hipError_t launch_affine_scan(const float* a, const float* b, float* oa, float* ob, int64_t rows, int64_t L,
+                              hipStream_t st);
+
+}  // namespace ssm

@@ -1,0 +1,115 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry
+point the public header declares, and rejects bad arguments before any HIP
+call.  Fake device addresses are used only in calls that must fail
+validation; none of them reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_ssm_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared_functions())
+    assert {"ssm_scan_fwd", "ssm_scan_fwd_plan", "ssm_scan_plan_for", "affine_scan", "affine_scan_order",
+            "ssm_last_error"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssm.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_affine_scan_order_constants():
+    o = ssm.affine_scan_order()
+    assert o == {"items_per_lane": 8, "lanes": 64, "waves": 4, "chunk": 8 * 64 * 4}
+
+
+# ------------------------------------------------------------ validation
+F = 0x100000  # fake, 16-byte aligned "device" addresses; never dereferenced
+
+
+def _fwd(**kw):
+    lib = ssm.load_library()
+    args = dict(u=F, delta=F * 2, A=F * 3, B=F * 4, C=F * 5, D=None, z=None, bias=None, sp=1, y=F * 8,
+                last=None, b=1, d=64, n=16, L=64, dtype=0, plan=0, S=0, chunk=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    rc = lib.ssm_scan_fwd_plan(P(args["u"]), P(args["delta"]), P(args["A"]), P(args["B"]), P(args["C"]),
+                               P(args["D"]), P(args["z"]), P(args["bias"]), args["sp"], P(args["y"]),
+                               P(args["last"]), args["b"], args["d"], args["n"], args["L"], args["dtype"],
+                               args["plan"], args["S"], args["chunk"], None)
+    return rc, lib.ssm_last_error().decode()
+
+
+# Addresses are spaced so that no tensor of these sizes overlaps another;
+# each case breaks exactly one rule.
+BIG = 1 << 30
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), ssm.SSM_EINVAL),
+    (dict(y=None), ssm.SSM_EINVAL),
+    (dict(b=0), ssm.SSM_EINVAL),
+    (dict(L=-1), ssm.SSM_EINVAL),
+    (dict(n=17), ssm.SSM_EUNSUPPORTED),
+    (dict(dtype=7), ssm.SSM_EUNSUPPORTED),
+    (dict(sp=2), ssm.SSM_EINVAL),
+    (dict(plan=9), ssm.SSM_EINVAL),
+    (dict(S=3), ssm.SSM_EINVAL),
+    (dict(chunk=100), ssm.SSM_EINVAL),
+    (dict(u=BIG + 4), ssm.SSM_EINVAL),          # misaligned
+    (dict(y=BIG), ssm.SSM_EINVAL, ),             # placeholder replaced below
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    base = dict(u=BIG, delta=2 * BIG, A=3 * BIG, B=4 * BIG, C=5 * BIG, y=8 * BIG)
+    base.update(kw)
+    if kw == dict(y=BIG):
+        base["y"] = base["u"] + 64  # y overlaps u
+    rc, msg = _fwd(**base)
+    assert rc == code, msg
+    assert msg
+
+
+def test_fwd_rejects_last_state_overlapping_y():
+    rc, msg = _fwd(u=BIG, delta=2 * BIG, A=3 * BIG, B=4 * BIG, C=5 * BIG, y=8 * BIG, last=8 * BIG + 256)
+    assert rc == ssm.SSM_EINVAL and "overlap" in msg
+
+
+def test_affine_scan_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    assert lib.affine_scan(None, P(BIG), None, P(2 * BIG), 4, 8, None) == ssm.SSM_EINVAL
+    assert lib.affine_scan(P(BIG), P(2 * BIG), None, P(3 * BIG), 0, 8, None) == ssm.SSM_EINVAL
+    assert lib.affine_scan(P(BIG + 8), P(2 * BIG), None, P(3 * BIG), 4, 8, None) == ssm.SSM_EINVAL
+    # out_b partially overlapping a
+    assert lib.affine_scan(P(BIG), P(2 * BIG), None, P(BIG + 16), 4, 8, None) == ssm.SSM_EINVAL
+    # out_a equal to b (not its own input)
+    assert lib.affine_scan(P(BIG), P(2 * BIG), P(2 * BIG), P(3 * BIG), 4, 8, None) == ssm.SSM_EINVAL
+
+
+def test_plan_choice():
+    # many channels: carry plan over the whole length
+    p = ssm.plan_for(8, 1536, 16, 2048)
+    assert p["plan"] == "carry" and p["chunk"] == 2048
+    p = ssm.plan_for(16, 5120, 16, 8192, "bf16")
+    assert p["plan"] == "carry"
+    # few channels, very long sequence: two-pass over chunks that are multiples of 64
+    p = ssm.plan_for(1, 2048, 16, 65536)
+    assert p["plan"] == "twopass" and p["chunk"] % 64 == 0 and 2 <= -(-65536 // p["chunk"]) <= 65535
+    # short sequence never splits
+    assert ssm.plan_for(1, 64, 16, 256)["plan"] == "carry"
+    with pytest.raises(ssm.SSMError):
+        ssm.plan_for(1, 64, 17, 256)
