@@ -1,0 +1,189 @@
+"""Benchmark: selective-scan forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 130m]
+
+One step is one ssm_scan_fwd call (the whole path: load, discretise, scan,
+C.h + D.u, gate, store) over one batch of the workload, inputs already
+resident in HBM.  The default workload is the Mamba-130m-like layer
+(b=8, d_inner=1536, d_state=16, L=2048, float32, gated).  Prints ONE JSON
+line.  Only one GPU is used: --gpus above 1 exits with a message.
+
+Reported:
+  value        algorithmic bytes / mean step time (GB/s); algorithmic bytes
+               = every input element once + y + last_state (no (a,b) pairs,
+               no per-step states).
+  hbm_frac     value / 8000 GB/s (MI355X HBM3E peak).
+  roofline     the binding roof of the scan kernel.  The recurrence costs, per
+               (channel, state, step), one v_exp_f32 (half rate on gfx950,
+               measured) plus two v_mul and two v_fma: 6 VALU issue slots.
+               MI355X issues 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz =
+               39.32e12 lane-slots/s without packed-FP32 instructions, so the
+               mix peaks at 39.32e12 / 6 state-steps/s; counting the mix as 7
+               FLOP (mul 1, exp 1, mul 1, fma 2, fma 2) that is 45.9 TFLOP/s.
+  cpu_baseline the float64 C oracle (OpenMP over channels) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9          # non-packed FP32 VALU issue
+SLOTS_PER_STATE_STEP = 6.0                      # exp (2 slots) + 2 mul + 2 fma
+FLOP_PER_STATE_STEP = 7.0
+ALU_PEAK_TFLOPS = LANE_SLOTS_PER_S / SLOTS_PER_STATE_STEP * FLOP_PER_STATE_STEP / 1e12
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="130m")
+    p.add_argument("--plan", default="auto")
+    p.add_argument("--states-per-wave", type=int, default=0)
+    p.add_argument("--chunk", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget for the CPU oracle baseline (0 disables it)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="per-launch HBM bytes measured with rocprofv3 counters, if present")
+    return p.parse_args()
+
+
+def cpu_baseline(inp, w, budget_s):
+    """The float64 C oracle, as it is, on a bounded sample of whole channels
+    of the same workload; throughput scaled to the workload's GB/s."""
+    import numpy as np
+    from oracle import build as ob, cpu
+    if not os.path.exists(ob.LIB):
+        ob.build()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    rows_total = w.batch * w.dim
+    host = {k: (v.float().cpu().numpy() if hasattr(v, "cpu") else v)
+            for k, v in inp.items() if k in ("u", "delta", "z", "A", "B", "C", "D", "delta_bias")}
+    rb_all = np.repeat(np.arange(w.batch), w.dim)
+    rd_all = np.tile(np.arange(w.dim), w.batch)
+
+    def run(nrows):
+        sel = np.linspace(0, rows_total - 1, nrows).astype(np.int64)
+        rb, rd = rb_all[sel], rd_all[sel]
+        pick = lambda x: None if x is None else np.ascontiguousarray(x[rb, rd])
+        t0 = time.perf_counter()
+        cpu.fwd_rows(pick(host["u"]), pick(host["delta"]), pick(host.get("z")), rb, rd, host["A"], host["B"],
+                     host["C"], host.get("D"), host.get("delta_bias"), w.softplus, w.batch, w.dim, w.dstate, w.L,
+                     nthreads=threads)
+        return time.perf_counter() - t0
+
+    # calibrate on a small sample, then size the timed sample to the budget
+    n0 = min(rows_total, max(threads, 64))
+    t_small = run(n0)
+    nrows = int(min(rows_total, max(n0, n0 * budget_s / max(t_small, 1e-6))))
+    elapsed = run(nrows)
+    frac = nrows / rows_total
+    gbs = w.algorithmic_bytes() * frac / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} of {rows_total} channels x {w.L} steps x {w.dstate} states "
+                      f"({elapsed:.1f} s, float64 C recurrence, OpenMP static over channels)",
+            "gsteps_ch_state_per_s": round(w.state_steps() * frac / elapsed / 1e9, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU scaling is not implemented "
+                                   "(see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import selective_state_space_ssm_amd as ssm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(w, device=dev, seed=0)
+    y = torch.empty_like(inp["u"])
+    last = torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32)
+    kw = dict(plan=args.plan, states_per_wave=args.states_per_wave, chunk=args.chunk, y=y, last_state=last)
+
+    def step():
+        ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                         inp["delta_bias"], delta_softplus=w.softplus, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms = sum(ev_ms) / len(ev_ms)
+    ms_wall = wall * 1e3 / args.steps
+
+    bytes_alg = w.algorithmic_bytes()
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    plan = ssm.plan_for(w.batch, w.dim, w.dstate, w.L, w.dtype)
+    if args.plan != "auto":
+        plan["plan"] = args.plan
+    tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f)
+            ent = tj.get(w.name)
+            if ent and ent.get("plan") == plan["plan"]:
+                traffic = ent.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": "selective-scan fwd GB/s (algorithmic bytes / step time)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "ms_per_step_wall": round(ms_wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and value recipes of the workload)",
+        "config": {"workload": w.name, "batch": w.batch, "d_inner": w.dim, "d_state": w.dstate, "seq_len": w.L,
+                   "io_dtype": w.dtype, "gated": w.gated, "plan": plan},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4), "traffic": traffic},
+        "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "algorithmic_bytes": bytes_alg},
+    }
+    if w.dtype == "bf16":
+        out["dtype"] = "f32 (bf16 storage)"
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

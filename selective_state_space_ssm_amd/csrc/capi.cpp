@@ -77,33 +77,30 @@ bool sg_instantiated(int S, int G) {
   }
 }
 
-// Plan choice.  The carry plan keeps one state vector per (channel, state
-// group) in registers for the whole length; it fills the GPU when there are
-// at least ~2 wavefronts per SIMD.  With too few channels for that, the
-// two-pass plan splits L into K chunks ([Scan page] §2.2: chunk aggregates,
-// a scan over the K chunk totals, then the fix-up) to multiply the number of
-// wavefronts by K.
+// Plan choice (measured on MI355X with the five benchmark workloads).  The
+// carry plan keeps one state vector per (channel, state group) in registers
+// for the whole length.  Four states per wave amortise the per-step prep,
+// gate and partial-sum work best and win whenever they still give about two
+// wavefronts per SIMD; otherwise two states per wave double the wavefronts.
+// With too few channels for even one wavefront per SIMD, the two-pass plan
+// splits L into K chunks ([Scan page] §2.2: chunk aggregates, a scan over
+// the K chunk totals, then the fix-up) to multiply the wavefronts by K.
 void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
   const int64_t blocks = batch * ceil_div(dim, 64);
   int S = 2;
-  for (int cand : {8, 4}) {
-    const int G = groups_for(dstate, cand);
-    if (!sg_instantiated(cand, G)) continue;
-    if (blocks * G >= 2 * kSimds) {
-      S = cand;
-      break;
-    }
-  }
+  if (blocks * groups_for(dstate, 4) >= 2 * kSimds && sg_instantiated(4, groups_for(dstate, 4))) S = 4;
   const int64_t waves = blocks * groups_for(dstate, S);
   int64_t chunk = L;
   int pl = SSM_PLAN_CARRY;
   if (waves < kSimds && L >= 2 * kMinChunk) {
-    int64_t K = ceil_div(2 * kSimds, waves);
+    const int S2 = sg_instantiated(4, groups_for(dstate, 4)) ? 4 : 2;
+    int64_t K = ceil_div(2 * kSimds, blocks * groups_for(dstate, S2));
     if (K > L / kMinChunk) K = L / kMinChunk;
     if (K > kMaxChunks) K = kMaxChunks;
     if (K >= 2) {
       chunk = ceil_div(ceil_div(L, K), 64) * 64;
       pl = SSM_PLAN_TWOPASS;
+      S = S2;
     }
   }
   if (plan) *plan = pl;

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ssm_kernels.h"
 
 namespace ssm {
@@ -118,14 +120,57 @@ __device__ __forceinline__ float silu(float zz) {
 }  // namespace
 
 // --------------------------------------------------------------------------
-// Channel-serial kernel.  Template: storage IO, states per wave S, waves G,
-// mode, and VEC (L % 4 == 0, so rows can be read in aligned 4-step vectors).
-// Grid: x = channel block (64 channels), y = batch row, z = chunk.
+// Broadcast of one step's B or C value: B and C for 16 consecutive steps sit
+// in one VGPR, lane j of every row of 16 lanes holding step j.  DPP
+// row_newbcast:j (gfx90a and later) hands lane j's value to its whole row as
+// the src0 operand of the consuming v_mul / v_fmac, at no extra instruction.
 // --------------------------------------------------------------------------
-// Every pointer is a separate __restrict__ parameter: the caller guarantees
-// outputs overlap no input, and with that knowledge the compiler keeps the
-// wave-uniform B/C reads as scalar loads even though y is stored in the loop.
-template <typename IO, int S, int G, int MODE, bool VEC>
+// x * bcast16<J>(c) and acc += bcast16<J>(c) * h as single v_mul_f32_dpp /
+// v_fmac_f32_dpp instructions, written out so that every mode gets the fused
+// form (the compiler folds a separate broadcast into v_mul only when both sit
+// in one basic block, and never into v_fmac).  Hazard: a DPP source must not
+// have been written by a VALU instruction in the two preceding instructions;
+// c is only ever written by memory loads, which tests/test_isa_hazards.py
+// checks on the generated ISA.
+template <int J>
+__device__ __forceinline__ float mul_bcast16(float c, float x) {
+  float r;
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=v"(r)
+      : "v"(c), "v"(x), "n"(J));
+  return r;
+}
+
+template <int J>
+__device__ __forceinline__ void fmac_bcast16(float& acc, float c, float h) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(acc)
+      : "v"(c), "v"(h), "n"(J));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Channel-serial kernel.  Template: storage IO, states per wave S, waves G,
+// mode, and GATED (z present).  Grid: x = channel block (64 channels),
+// y = batch row, z = chunk.  Every pointer is a separate __restrict__
+// parameter: the caller guarantees that outputs overlap no input.
+//
+// Two code paths share the registers and LDS layout:
+//  * fast: a full block of 64 channels, whole tiles, L % 4 == 0.  The loop
+//    body is straight-line (next-tile prefetches use clamped addresses
+//    instead of branches), so the compiler can count outstanding memory
+//    operations exactly and wait only for the ones each step consumes.
+//  * generic: any tail tile, a partial channel block or unaligned L; loads
+//    and stores element by element with bounds checks, no prefetch.
+// --------------------------------------------------------------------------
+template <typename IO, int S, int G, int MODE, bool GATED>
 __global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
     const typename IO::T* __restrict__ u, const typename IO::T* __restrict__ dlt,
     const float* __restrict__ Ag, const typename IO::T* __restrict__ Bg, const typename IO::T* __restrict__ Cg,
@@ -134,16 +179,22 @@ __global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
     float* __restrict__ agg_p, float* __restrict__ agg_h, CsSizes p) {
   using T = typename IO::T;
   constexpr int kThreads = 64 * G;
-  constexpr int kSlotsPerThread = (kSlots + kThreads - 1) / kThreads;
+  constexpr int kSPT = (kSlots + kThreads - 1) / kThreads;  // prep/epilogue slots per thread
+  constexpr bool kEvenSlots = (kSlots % kThreads) == 0;
+  constexpr int kH = kTT / 16;                               // 16-step halves per tile
+  constexpr bool kGate = GATED && MODE == kFull;
+  constexpr int kNS = S * G;                                 // state rows staged per tile
+  constexpr int kBCq = 2 * kNS * kQ4;                        // 4-step B/C groups per tile
+  constexpr int kBCPT = (kBCq + kThreads - 1) / kThreads;    // ... per thread
 
   extern __shared__ float smem[];
   float* sDt = smem;                 // [64][kRow]  Delta2
   float* sDu = sDt + kCH * kRow;     // [64][kRow]  Delta * u
-  float* sY = sDu + kCH * kRow;      // [G][64][kRow] partial y (kFull only)
+  float* sBC = sDu + kCH * kRow;     // [2][kNS][kTT] B and C of the tile, float32 (fast path)
+  float* sY = sBC + 2 * kNS * kTT;   // [G][64][kRow] partial y (kFull only)
 
   const int tid = threadIdx.x;
-  // wave index as an SGPR: every per-wave quantity below (state indices,
-  // B/C row addresses) is then uniform and B/C become scalar loads
+  // the wave index as an SGPR keeps every per-wave quantity uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int64_t dim = p.dim, L = p.L, N = p.dstate;
@@ -153,7 +204,6 @@ __global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
   const int64_t t_begin = k * p.chunk;
   const int64_t t_end = (t_begin + p.chunk < L) ? t_begin + p.chunk : L;
   const bool softplus = p.softplus != 0;
-  const bool gated = (MODE == kFull) && zg != nullptr;
 
   // ---- recurrence registers: S states of channel d0 + lane
   const int64_t d = d0 + lane;
@@ -177,9 +227,9 @@ __global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
   float dsum = 0.0f;  // kAgg: sum of Delta2 over the chunk
 
   // ---- prep/epilogue slots of this thread: (row, 4-step group)
-  float bias2[kSlotsPerThread], Dd[kSlotsPerThread];
+  float bias2[kSPT], Dd[kSPT];
 #pragma unroll
-  for (int j = 0; j < kSlotsPerThread; ++j) {
+  for (int j = 0; j < kSPT; ++j) {
     const int q = tid + j * kThreads;
     const int64_t dd = d0 + q / kQ4;
     const bool ok = q < kSlots && dd < dim;
@@ -187,156 +237,234 @@ __global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
     Dd[j] = (ok && Dg) ? Dg[dd] : 0.0f;
   }
 
-  // raw inputs of the tile being prepared (prefetched one tile ahead)
-  float4 ru[kSlotsPerThread], rd[kSlotsPerThread], rz[kSlotsPerThread];
+  const float* rowDt = sDt + lane * kRow;
+  const float* rowDu = sDu + lane * kRow;
+  float* rowY = sY + (wave * kCH + lane) * kRow;
 
-  auto fetch = [&](int64_t t0) {
+  // Reduce the G partial sums of one slot, add D*u, gate, store (fast path).
+  auto epilogue_slot = [&](int j, int64_t t0, float4 uu, float4 zz, bool vec) {
+    const int q = tid + j * kThreads;
+    const int r = q / kQ4;
+    const int c4 = (q % kQ4) * 4;
+    float4 acc = *reinterpret_cast<const float4*>(sY + r * kRow + c4);
 #pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) {
-      const int q = tid + j * kThreads;
-      const int r = q / kQ4;
-      const int64_t dd = d0 + r;
-      const int64_t t = t0 + (q % kQ4) * 4;
-      ru[j] = rd[j] = rz[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (q >= kSlots || dd >= dim) continue;
-      const int64_t off = (b * dim + dd) * L + t;
-      if (VEC && t + 4 <= t_end) {
-        ru[j] = IO::ld4(u + off);
-        rd[j] = IO::ld4(dlt + off);
-        if (gated) rz[j] = IO::ld4(zg + off);
-      } else {
+    for (int g = 1; g < G; ++g) {
+      const float4 v = *reinterpret_cast<const float4*>(sY + (g * kCH + r) * kRow + c4);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    float4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (t + e < t_end) {
-            set(ru[j], e, IO::ld1(u + off + e));
-            set(rd[j], e, IO::ld1(dlt + off + e));
-            if (gated) set(rz[j], e, IO::ld1(zg + off + e));
-          }
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      float yv = __builtin_fmaf(Dd[j], get(uu, e), get(acc, e));
+      if (kGate) yv = yv * silu(get(zz, e));
+      set(out, e, yv);
+    }
+    const int64_t dd = d0 + r;
+    const int64_t t = t0 + c4;
+    const int64_t off = (b * dim + dd) * L + t;
+    if (vec) {
+      IO::st4(yg + off, out);
+    } else if (dd < dim) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (t + e < t_end) IO::st1(yg + off + e, get(out, e));
     }
   };
 
-  float4 pu[kSlotsPerThread], pz[kSlotsPerThread];  // u, z of the tile in flight
-
-  if (t_begin < t_end) fetch(t_begin);
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
-    const int nsteps = static_cast<int>((t_end - t0 < kTT) ? (t_end - t0) : kTT);
-
-    // ---------------- prep: Delta2 and Delta*u into LDS
+  // ======================== fast path ========================
+  const bool fast = (L % 4 == 0) && (d0 + kCH <= dim) && kEvenSlots;
+  const int64_t n_fast = fast ? (t_end - t_begin) / kTT : 0;
+  const int64_t t_fast_end = t_begin + n_fast * kTT;
+  if (n_fast > 0) {
+    // raw inputs of the next tile, prefetched one tile ahead
+    float4 ru[kSPT], rd[kSPT], rz[kSPT], rbc[kBCPT];
+    auto fetch = [&](int64_t t0) {
 #pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) {
-      const int q = tid + j * kThreads;
-      if (q >= kSlots) continue;
-      const int r = q / kQ4;
-      const int c4 = (q % kQ4) * 4;
-      const int64_t t = t0 + c4;
-      float4 dt, du;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool live = t + e < t_end && d0 + r < dim;
-        const float v2 = live ? delta2(get(rd[j], e), bias2[j], softplus) : 0.0f;
-        set(dt, e, v2);
-        set(du, e, live ? (v2 * kLn2) * get(ru[j], e) : 0.0f);
+      for (int j = 0; j < kSPT; ++j) {
+        const int q = tid + j * kThreads;
+        const int64_t off = (b * dim + d0 + q / kQ4) * L + t0 + (q % kQ4) * 4;
+        ru[j] = IO::ld4(u + off);
+        rd[j] = IO::ld4(dlt + off);
+        if (kGate) rz[j] = IO::ld4(zg + off);
       }
-      *reinterpret_cast<float4*>(sDt + r * kRow + c4) = dt;
-      *reinterpret_cast<float4*>(sDu + r * kRow + c4) = du;
-      pu[j] = ru[j];
-      pz[j] = rz[j];
-    }
-    // issue the next tile's loads; they complete during the recurrence
-    if (t0 + kTT < t_end) fetch(t0 + kTT);
-    __syncthreads();
-
-    // ---------------- recurrence over this tile
-    const float* rowDt = sDt + lane * kRow;
-    const float* rowDu = sDu + lane * kRow;
-    float* rowY = sY + (wave * kCH + lane) * kRow;
-    if (VEC && nsteps == kTT) {
-      // Unroll depth bounds the scalar loads in flight: 2*S*4 SGPRs per group.
-#pragma unroll (S <= 2 ? kQ4 : (S == 4 ? 2 : 1))
-      for (int g4 = 0; g4 < kQ4; ++g4) {
-        const float4 dt4 = *reinterpret_cast<const float4*>(rowDt + g4 * 4);
-        const float4 du4 = *reinterpret_cast<const float4*>(rowDu + g4 * 4);
-        float4 bq[S], cq[S];
+      // B then C rows of every staged state; rows past d_state read row 0
+      // and are zeroed when written to LDS.  Every thread issues its loads
+      // (surplus threads re-read a valid group) so that the number of memory
+      // operations in flight is the same on every path.
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          if (svalid[s]) {
-            bq[s] = IO::ld4(Brow[s] + t0 + g4 * 4);
-            cq[s] = (MODE == kFull) ? IO::ld4(Crow[s] + t0 + g4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-          } else {
-            bq[s] = cq[s] = make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-        float4 y4;
+      for (int j = 0; j < kBCPT; ++j) {
+        const int q = (tid + j * kThreads) % kBCq;
+        const int row = q / kQ4;                    // 0..2*kNS-1
+        const int n = row % kNS;
+        const T* base = (row < kNS) ? Bg : Cg;
+        const int64_t nn = (n < N) ? n : 0;
+        rbc[j] = IO::ld4(base + (b * N + nn) * L + t0 + (q % kQ4) * 4);
+      }
+    };
+
+    float4 pu[kSPT], pz[kSPT];  // u, z of the tile whose epilogue is pending
+
+    // ---- prep: Delta2, Delta*u, B, C of the tile in registers into LDS
+    auto prep = [&]() {
+#pragma unroll
+      for (int j = 0; j < kSPT; ++j) {
+        const int q = tid + j * kThreads;
+        const int r = q / kQ4;
+        const int c4 = (q % kQ4) * 4;
+        float4 dt, du;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float dt = get(dt4, e), du = get(du4, e);
+          const float v2 = delta2(get(rd[j], e), bias2[j], softplus);
+          set(dt, e, v2);
+          set(du, e, (v2 * kLn2) * get(ru[j], e));
+        }
+        *reinterpret_cast<float4*>(sDt + r * kRow + c4) = dt;
+        *reinterpret_cast<float4*>(sDu + r * kRow + c4) = du;
+        pu[j] = ru[j];
+        pz[j] = rz[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kBCPT; ++j) {
+        const int q = tid + j * kThreads;
+        if (kBCq % kThreads != 0 && q >= kBCq) continue;
+        const int row = q / kQ4;
+        const bool ok = (row % kNS) < N && (MODE == kFull || row < kNS);
+        *reinterpret_cast<float4*>(sBC + row * kTT + (q % kQ4) * 4) =
+            ok ? rbc[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+
+    // ---- recurrence of one tile from LDS
+    auto recur = [&]() {
+      float4 dq[kQ4], uq[kQ4];
+      float bc[S][kH], cc[S][kH];  // lane l: step 16*half + (l & 15) of state wave*S+s
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int hh = 0; hh < kH; ++hh) {
+          const int n = wave * S + s;
+          bc[s][hh] = sBC[n * kTT + 16 * hh + (lane & 15)];
+          cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + 16 * hh + (lane & 15)] : 0.0f;
+        }
+#pragma unroll
+      for (int g4 = 0; g4 < kQ4; ++g4) {
+        dq[g4] = *reinterpret_cast<const float4*>(rowDt + g4 * 4);
+        uq[g4] = *reinterpret_cast<const float4*>(rowDu + g4 * 4);
+      }
+      static_for<0, kH>([&](auto HH) {
+        constexpr int hh = decltype(HH)::value;
+        float4 y4;
+        static_for<0, 16>([&](auto JJ) {
+          constexpr int j = decltype(JJ)::value;
+          constexpr int st = hh * 16 + j;
+          const float dt = get(dq[st / 4], st % 4);
+          const float du = get(uq[st / 4], st % 4);
           float yv = 0.0f;
 #pragma unroll
           for (int s = 0; s < S; ++s) {
             const float a = __builtin_amdgcn_exp2f(dt * An[s]);
-            h[s] = __builtin_fmaf(a, h[s], du * get(bq[s], e));
-            if (MODE == kFull) yv = (s == 0) ? get(cq[s], e) * h[s] : __builtin_fmaf(get(cq[s], e), h[s], yv);
+            h[s] = __builtin_fmaf(a, h[s], mul_bcast16<j>(bc[s][hh], du));
+            if (MODE == kFull) {
+              if (s == 0)
+                yv = mul_bcast16<j>(cc[s][hh], h[s]);
+              else
+                fmac_bcast16<j>(yv, cc[s][hh], h[s]);
+            }
           }
           if (MODE == kAgg) dsum += dt;
-          set(y4, e, yv);
-        }
-        if (MODE == kFull) *reinterpret_cast<float4*>(rowY + g4 * 4) = y4;
-      }
-    } else {
-      for (int e = 0; e < nsteps; ++e) {
-        const float dt = rowDt[e], du = rowDu[e];
-        float yv = 0.0f;
+          set(y4, j % 4, yv);
+          if (MODE == kFull && j % 4 == 3) *reinterpret_cast<float4*>(rowY + st - 3) = y4;
+        });
+      });
+    };
+
+    auto epilogue = [&](int64_t t0) {
+      if (MODE == kFull) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const float bv = svalid[s] ? IO::ld1(Brow[s] + t0 + e) : 0.0f;
-          const float cv = (MODE == kFull && svalid[s]) ? IO::ld1(Crow[s] + t0 + e) : 0.0f;
-          const float a = __builtin_amdgcn_exp2f(dt * An[s]);
-          h[s] = __builtin_fmaf(a, h[s], du * bv);
-          if (MODE == kFull) yv = (s == 0) ? cv * h[s] : __builtin_fmaf(cv, h[s], yv);
+        for (int j = 0; j < kSPT; ++j) epilogue_slot(j, t0, pu[j], pz[j], true);
+      }
+    };
+
+    // Tile 0 is peeled and every later iteration starts with the previous
+    // tile's epilogue: the loop is entered from both sides with the same
+    // memory operations outstanding (the prefetched loads are the newest),
+    // so waits are counted exactly and never include the y stores.
+    fetch(t_begin);
+    prep();
+    fetch(n_fast > 1 ? t_begin + kTT : t_begin);
+    __syncthreads();
+    recur();
+    __syncthreads();
+    for (int64_t it = 1; it < n_fast; ++it) {
+      const int64_t t0 = t_begin + it * kTT;
+      const int64_t tn = (it + 1 < n_fast) ? t0 + kTT : t0;
+      epilogue(t0 - kTT);
+      prep();
+      fetch(tn);
+      __syncthreads();
+      recur();
+      __syncthreads();
+    }
+    epilogue(t_fast_end - kTT);
+  }
+
+  // ======================== generic path ========================
+  for (int64_t t0 = t_fast_end; t0 < t_end; t0 += kTT) {
+    const int nsteps = static_cast<int>((t_end - t0 < kTT) ? (t_end - t0) : kTT);
+    float4 pu[kSPT], pz[kSPT];
+#pragma unroll
+    for (int j = 0; j < kSPT; ++j) {
+      const int q = tid + j * kThreads;
+      pu[j] = pz[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q >= kSlots) continue;
+      const int r = q / kQ4;
+      const int c4 = (q % kQ4) * 4;
+      const int64_t dd = d0 + r;
+      const int64_t t = t0 + c4;
+      float4 dt = make_float4(0.f, 0.f, 0.f, 0.f), du = dt;
+      if (dd < dim) {
+        const int64_t off = (b * dim + dd) * L + t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (t + e < t_end) {
+            const float uu = IO::ld1(u + off + e);
+            const float v2 = delta2(IO::ld1(dlt + off + e), bias2[j], softplus);
+            set(dt, e, v2);
+            set(du, e, (v2 * kLn2) * uu);
+            set(pu[j], e, uu);
+            if (kGate) set(pz[j], e, IO::ld1(zg + off + e));
+          }
         }
-        if (MODE == kAgg) dsum += dt;
-        if (MODE == kFull) rowY[e] = yv;
+      }
+      *reinterpret_cast<float4*>(sDt + r * kRow + c4) = dt;
+      *reinterpret_cast<float4*>(sDu + r * kRow + c4) = du;
+    }
+    __syncthreads();
+    for (int e = 0; e < nsteps; ++e) {
+      const float dt = rowDt[e], du = rowDu[e];
+      float yv = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float bv = svalid[s] ? IO::ld1(Brow[s] + t0 + e) : 0.0f;
+        const float cv = (MODE == kFull && svalid[s]) ? IO::ld1(Crow[s] + t0 + e) : 0.0f;
+        const float a = __builtin_amdgcn_exp2f(dt * An[s]);
+        h[s] = __builtin_fmaf(a, h[s], du * bv);
+        if (MODE == kFull) yv = (s == 0) ? cv * h[s] : __builtin_fmaf(cv, h[s], yv);
+      }
+      if (MODE == kAgg) dsum += dt;
+      if (MODE == kFull) rowY[e] = yv;
+    }
+    __syncthreads();
+    if (MODE == kFull) {
+#pragma unroll
+      for (int j = 0; j < kSPT; ++j) {
+        const int q = tid + j * kThreads;
+        if (q >= kSlots) continue;
+        if (t0 + (q % kQ4) * 4 >= t_end) continue;
+        epilogue_slot(j, t0, pu[j], pz[j], false);
       }
     }
     __syncthreads();
-
-    // ---------------- epilogue: reduce partial sums, D skip, gate, store
-    if (MODE == kFull) {
-#pragma unroll
-      for (int j = 0; j < kSlotsPerThread; ++j) {
-        const int q = tid + j * kThreads;
-        if (q >= kSlots) continue;
-        const int r = q / kQ4;
-        const int c4 = (q % kQ4) * 4;
-        const int64_t dd = d0 + r;
-        const int64_t t = t0 + c4;
-        if (dd >= dim || t >= t_end) continue;
-        float4 acc = *reinterpret_cast<const float4*>(sY + r * kRow + c4);
-#pragma unroll
-        for (int g = 1; g < G; ++g) {
-          const float4 v = *reinterpret_cast<const float4*>(sY + (g * kCH + r) * kRow + c4);
-          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
-        float4 out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float yv = __builtin_fmaf(Dd[j], get(pu[j], e), get(acc, e));
-          if (gated) yv = yv * silu(get(pz[j], e));
-          set(out, e, yv);
-        }
-        const int64_t off = (b * dim + dd) * L + t;
-        if (VEC && t + 4 <= t_end) {
-          IO::st4(yg + off, out);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (t + e < t_end) IO::st1(yg + off + e, get(out, e));
-        }
-      }
-    }
   }
 
   // ---- chunk end: final state or chunk aggregate
@@ -377,19 +505,20 @@ __global__ __launch_bounds__(256) void ssm_combine_kernel(const float* __restric
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
-size_t cs_smem_bytes(int G, int mode) {
-  return sizeof(float) * static_cast<size_t>(kCH) * kRow * (2 + (mode == kFull ? G : 0));
+size_t cs_smem_bytes(int S, int G, int mode) {
+  return sizeof(float) * (static_cast<size_t>(kCH) * kRow * (2 + (mode == kFull ? G : 0)) +
+                          static_cast<size_t>(2) * S * G * kTT);
 }
 
 int cs_time_tile() { return kTT; }
 
-template <typename IO, int S, int G, int MODE, bool VEC>
+template <typename IO, int S, int G, int MODE, bool GATED>
 static hipError_t launch_cs_v(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
   using T = typename IO::T;
   const dim3 grid(static_cast<unsigned>((a.dim + kCH - 1) / kCH), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(nchunks));
-  const size_t smem = cs_smem_bytes(G, MODE);
-  auto kern = ssm_cs_kernel<IO, S, G, MODE, VEC>;
+  const size_t smem = cs_smem_bytes(S, G, MODE);
+  auto kern = ssm_cs_kernel<IO, S, G, MODE, GATED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
@@ -403,8 +532,8 @@ static hipError_t launch_cs_v(const FwdArgs& a, int64_t nchunks, hipStream_t st)
 
 template <typename IO, int S, int G, int MODE>
 static hipError_t launch_cs(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
-  return (a.L % 4 == 0) ? launch_cs_v<IO, S, G, MODE, true>(a, nchunks, st)
-                        : launch_cs_v<IO, S, G, MODE, false>(a, nchunks, st);
+  if (MODE == kFull && a.z != nullptr) return launch_cs_v<IO, S, G, MODE, true>(a, nchunks, st);
+  return launch_cs_v<IO, S, G, MODE, false>(a, nchunks, st);
 }
 
 template <typename IO, int MODE>

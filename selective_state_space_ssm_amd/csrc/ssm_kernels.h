@@ -35,7 +35,7 @@ struct CsSizes {
   int softplus;
 };
 
-size_t cs_smem_bytes(int G, int mode);
+size_t cs_smem_bytes(int S, int G, int mode);
 int cs_time_tile();
 hipError_t launch_cs_full(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);
 hipError_t launch_cs_agg(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);

@@ -1,0 +1,88 @@
+"""Static check of the generated gfx950 ISA for the one hazard the compiler
+cannot see: the inline-asm v_mul_f32_dpp / v_fmac_f32_dpp read their DPP
+source (src0) through a cross-lane broadcast, and gfx9 requires two wait
+states between a VALU write of a VGPR and a DPP read of it.  The kernels
+keep those sources load-only; this test compiles ssm_fwd.hip to assembly
+(CPU only) and fails if any VALU instruction writes the source of any DPP
+instruction within the two instructions before it, or if standalone
+broadcasts (v_mov_b32_dpp, one extra instruction per state-step) appear."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "selective_state_space_ssm_amd", "csrc")
+
+pytestmark = pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def isa(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "ssm_fwd.s"
+    cmd = ["/opt/rocm/bin/hipcc", "-O3", "--offload-arch=gfx950", "-std=c++17", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, "ssm_fwd.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _instructions(text):
+    """(mnemonic, operand string) per instruction line, labels and directives dropped."""
+    out = []
+    for line in text.splitlines():
+        line = line.split(";")[0].strip()
+        if not line or line.endswith(":") or line.startswith(".") or line.startswith("#"):
+            continue
+        parts = line.split(None, 1)
+        out.append((parts[0], parts[1] if len(parts) > 1 else ""))
+    return out
+
+
+def _regs(operand):
+    """VGPR indices named by one operand (v7 or v[4:7])."""
+    m = re.fullmatch(r"v(\d+)", operand)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def test_dpp_sources_not_written_by_valu_just_before(isa):
+    ins = _instructions(isa)
+    checked = 0
+    for i, (op, args) in enumerate(ins):
+        if not op.endswith("_dpp") or "row_newbcast" not in args:
+            continue
+        src0 = args.split(",")[1].strip()
+        regs = _regs(src0)
+        assert regs, args
+        # the two instructions before (s_nop n counts as n+1 wait states)
+        waits = 0
+        j = i - 1
+        while j >= 0 and waits < 2:
+            pop, pargs = ins[j]
+            if pop == "s_nop":
+                waits += int(pargs.strip() or 0) + 1
+                j -= 1
+                continue
+            if pop.startswith("v_") and not pop.startswith("v_cmp") and not pop.startswith("v_readlane") \
+                    and not pop.startswith("v_readfirstlane"):
+                dst = pargs.split(",")[0].strip()
+                assert not (_regs(dst) & regs), f"VALU write of DPP source {src0} right before: {pop} {pargs}"
+            waits += 1
+            j -= 1
+        checked += 1
+    assert checked > 0
+
+
+def test_row_broadcasts_are_fused(isa):
+    """Almost every per-step B/C broadcast is an operand of the consuming
+    v_mul/v_fmac; a stray standalone broadcast costs one instruction."""
+    ins = _instructions(isa)
+    fused = sum(1 for op, a in ins if "row_newbcast" in a and op != "v_mov_b32_dpp")
+    loose = sum(1 for op, a in ins if "row_newbcast" in a and op == "v_mov_b32_dpp")
+    assert fused > 0 and loose == 0, (fused, loose)
