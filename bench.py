@@ -48,13 +48,69 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="130m")
     p.add_argument("--plan", default="auto")
-    p.add_argument("--states-per-wave", type=int, default=0)
+    p.add_argument("--states-per-lane", type=int, default=0)
     p.add_argument("--chunk", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget for the CPU oracle baseline (0 disables it)")
-    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                   help="per-launch HBM bytes measured with rocprofv3 counters, if present")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
+                        "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+METRIC = "selective-scan fwd GB/s and % of MI355X HBM peak; Gsteps\u00b7ch\u00b7state/s"
+COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibration copy
+
+# HBM bytes per launch of the scan kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), each multiplied by the factor that maps the
+# same counter to the known byte count of a plain device copy (bench.py
+# --calibrate-copy).  Keyed by workload; valid only for the kernel sources
+# whose digest is stored with it (any change to them makes the figure stale,
+# and it is reported as null).  The summaries these come from are the
+# profiles/*counters*.md files.
+MEASURED_TRAFFIC = {}
+
+
+def kernel_digest() -> str:
+    """sha256 over the HIP sources and build flags of the library."""
+    import hashlib
+    pkg = os.path.join(ROOT, "selective_state_space_ssm_amd")
+    h = hashlib.sha256()
+    for sub in ("csrc", ""):
+        d = os.path.join(pkg, sub)
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".cpp")) or name == "build.py":
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, plan: dict):
+    ent = MEASURED_TRAFFIC.get(workload)
+    if not ent or ent.get("digest") != kernel_digest() or ent.get("plan") != plan.get("plan"):
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
+
+
+def calibrate_copy(args):
+    """A plain device-to-device copy of COPY_BYTES, launched --steps times, so
+    that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE can be read for a kernel
+    whose HBM traffic is known exactly (COPY_BYTES read, COPY_BYTES written)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.randn(COPY_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(2 * COPY_BYTES / ms / 1e6, 1)}),
+          flush=True)
 
 
 def cpu_baseline(inp, w, budget_s):
@@ -100,6 +156,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU scaling is not implemented "
                                    "(see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return
     import torch
 
     import selective_state_space_ssm_amd as ssm
@@ -113,7 +172,7 @@ def main():
     inp = workloads.make_inputs(w, device=dev, seed=0)
     y = torch.empty_like(inp["u"])
     last = torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32)
-    kw = dict(plan=args.plan, states_per_wave=args.states_per_wave, chunk=args.chunk, y=y, last_state=last)
+    kw = dict(plan=args.plan, states_per_lane=args.states_per_lane, chunk=args.chunk, y=y, last_state=last)
 
     def step():
         ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
@@ -143,19 +202,9 @@ def main():
     if args.plan != "auto":
         plan["plan"] = args.plan
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            ent = tj.get(w.name)
-            if ent and ent.get("plan") == plan["plan"]:
-                traffic = ent.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
-
+    traffic = measured_traffic(w.name, plan)
     out = {
-        "metric": "selective-scan fwd GB/s (algorithmic bytes / step time)",
+        "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -98,8 +98,10 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
  * ssm_scan_fwd_plan -- ssm_scan_fwd with an explicit plan
  * ([Scan page] §2.2 and §3.3 describe both decompositions).
  *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY or SSM_PLAN_TWOPASS.
- *   states_per_wave : how many of the d_state states one wavefront carries
- *                     per channel (2, 4 or 8; 0 = automatic).
+ *   states_per_lane : how many of the d_state states one lane carries for
+ *                     its channel (1, 2 or 4; 0 = automatic).  A workgroup
+ *                     covers 16 channels and 16 states with 4/states_per_lane
+ *                     wavefronts.
  *   chunk           : two-pass chunk length in steps, a multiple of 64
  *                     (0 = automatic; ignored by the carry plan).
  * Same semantics, arguments and errors as ssm_scan_fwd otherwise; results of
@@ -109,7 +111,7 @@ int ssm_scan_fwd_plan(const void *u, const void *delta, const float *A, const vo
                       const float *D, const void *z, const float *delta_bias, int delta_softplus,
                       void *y, float *last_state,
                       int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
-                      int dtype, int plan, int states_per_wave, int64_t chunk, void *stream);
+                      int dtype, int plan, int states_per_lane, int64_t chunk, void *stream);
 
 /*
  * ssm_scan_plan_for -- the plan, states per wave and chunk length that
@@ -117,7 +119,7 @@ int ssm_scan_fwd_plan(const void *u, const void *delta, const float *A, const vo
  * Any output pointer may be NULL.  Returns SSM_OK or SSM_EINVAL.
  */
 int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
-                      int *plan, int *states_per_wave, int64_t *chunk);
+                      int *plan, int *states_per_lane, int64_t *chunk);
 
 /*
  * affine_scan -- inclusive scan of affine pairs along each row

@@ -100,7 +100,7 @@ def _stream(device) -> ctypes.c_void_p:
 def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                  D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
-                 return_last_state: bool = True, plan: str = "auto", states_per_wave: int = 0,
+                 return_last_state: bool = True, plan: str = "auto", states_per_lane: int = 0,
                  chunk: int = 0, y: Optional[torch.Tensor] = None,
                  last_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective-scan forward on the GPU (see ``ssm_scan_fwd`` in include/ssm_scan.h).
@@ -145,7 +145,7 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
         rc = lib.ssm_scan_fwd_plan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                    _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
                                    bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16,
-                                   PLANS[plan], int(states_per_wave), int(chunk), _stream(device))
+                                   PLANS[plan], int(states_per_lane), int(chunk), _stream(device))
     _check(rc)
     return y, last_state
 
@@ -195,4 +195,4 @@ def plan_for(batch: int, d_inner: int, d_state: int, L: int, dtype=torch.float32
     code = SSM_F32 if dtype in (torch.float32, "f32") else SSM_BF16
     _check(lib.ssm_scan_plan_for(batch, d_inner, d_state, L, code, ctypes.byref(pl), ctypes.byref(s),
                                  ctypes.byref(ch)))
-    return {"plan": _PLAN_NAMES[pl.value], "states_per_wave": s.value, "chunk": ch.value}
+    return {"plan": _PLAN_NAMES[pl.value], "states_per_lane": s.value, "chunk": ch.value}

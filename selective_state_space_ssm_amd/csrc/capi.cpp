@@ -53,54 +53,45 @@ bool mul_ok(int64_t x, int64_t y, int64_t* out) {
   return true;
 }
 
-constexpr int kSimds = 256 * 4;    // MI355X: 256 CUs x 4 SIMDs
+constexpr int64_t kCUs = 256;      // MI355X: 256 CUs of 4 SIMDs
 constexpr int64_t kMaxChunks = 65535;
 constexpr int64_t kMinChunk = 1024;
+constexpr int64_t kGroup = 16;     // channels per workgroup
+// Longest L: 16 rows of float32 (the rows of one workgroup, or the d_state
+// rows of B or C) stay below 2^32 bytes with room for the read-ahead.
+constexpr int64_t kMaxL = ((int64_t(1) << 32) - 4096) / (16 * 4);
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves per state group count G for S states per wave (G is rounded up to a
-// power of two that the kernels are instantiated for).
-int groups_for(int64_t dstate, int S) {
-  int64_t g = ceil_div(dstate, S);
-  int G = 1;
-  while (G < g) G *= 2;
-  return G;
-}
+// Plan choice, measured on MI355X with the five benchmark workloads.
+//  * States per lane S: the workgroup covers 16 channels x 16 states with
+//    4/S wavefronts.  Four states per lane spend the fewest issue slots per
+//    state-step (fewest partial sums to add) and win when every SIMD still
+//    gets two or more wavefronts (six or more workgroups per CU).  With fewer
+//    channels, two states per lane double the wavefronts; one state per lane
+//    would triple them but doubles the LDS traffic per state-step, which
+//    measured slower at every benchmark shape.
+//  * Carry vs two-pass: the carry plan keeps one state vector per (channel,
+//    state) in registers for the whole length.  With fewer workgroups than
+//    CUs and a long sequence, the two-pass plan splits L into K chunks
+//    ([Scan page] §2.2: chunk aggregates, a scan over the K chunk totals,
+//    then the fix-up) so that about eight workgroups run per CU.
+int states_for(int64_t wgs) { return wgs >= 6 * kCUs ? 4 : 2; }
 
-bool sg_instantiated(int S, int G) {
-  switch (S) {
-    case 2: return G == 1 || G == 2 || G == 4 || G == 8;
-    case 4: return G == 1 || G == 2 || G == 4;
-    case 8: return G == 1 || G == 2;
-    default: return false;
-  }
-}
-
-// Plan choice (measured on MI355X with the five benchmark workloads).  The
-// carry plan keeps one state vector per (channel, state group) in registers
-// for the whole length.  Four states per wave amortise the per-step prep,
-// gate and partial-sum work best and win whenever they still give about two
-// wavefronts per SIMD; otherwise two states per wave double the wavefronts.
-// With too few channels for even one wavefront per SIMD, the two-pass plan
-// splits L into K chunks ([Scan page] §2.2: chunk aggregates, a scan over
-// the K chunk totals, then the fix-up) to multiply the wavefronts by K.
 void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
-  const int64_t blocks = batch * ceil_div(dim, 64);
-  int S = 2;
-  if (blocks * groups_for(dstate, 4) >= 2 * kSimds && sg_instantiated(4, groups_for(dstate, 4))) S = 4;
-  const int64_t waves = blocks * groups_for(dstate, S);
+  (void)dstate;
+  const int64_t groups = batch * ceil_div(dim, kGroup);
   int64_t chunk = L;
   int pl = SSM_PLAN_CARRY;
-  if (waves < kSimds && L >= 2 * kMinChunk) {
-    const int S2 = sg_instantiated(4, groups_for(dstate, 4)) ? 4 : 2;
-    int64_t K = ceil_div(2 * kSimds, blocks * groups_for(dstate, S2));
+  int S = states_for(groups);
+  if (groups < kCUs && L >= 2 * kMinChunk) {
+    int64_t K = ceil_div(8 * kCUs, groups);
     if (K > L / kMinChunk) K = L / kMinChunk;
     if (K > kMaxChunks) K = kMaxChunks;
     if (K >= 2) {
       chunk = ceil_div(ceil_div(L, K), 64) * 64;
       pl = SSM_PLAN_TWOPASS;
-      S = S2;
+      S = states_for(groups * ceil_div(L, chunk));
     }
   }
   if (plan) *plan = pl;
@@ -114,6 +105,9 @@ int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t L) {
                 (long long)batch, (long long)dim, (long long)dstate, (long long)L);
   if (dstate > 16) return fail(SSM_EUNSUPPORTED, "d_state=%lld > 16 is not supported", (long long)dstate);
   if (batch > 65535) return fail(SSM_EUNSUPPORTED, "batch=%lld > 65535 is not supported", (long long)batch);
+  if (L > kMaxL)
+    return fail(SSM_EUNSUPPORTED, "L=%lld exceeds %lld (a workgroup's 16 rows are addressed with 32-bit byte offsets)",
+                (long long)L, (long long)kMaxL);
   int64_t bd, bdl, bnl;
   if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, L, &bdl) || !mul_ok(batch * dstate, L, &bnl) || bdl > (int64_t(1) << 60))
     return fail(SSM_EINVAL, "tensor sizes overflow");
@@ -132,8 +126,8 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
   if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS)
     return fail(SSM_EINVAL, "unknown plan %d", plan);
-  if (S_req != 0 && S_req != 2 && S_req != 4 && S_req != 8)
-    return fail(SSM_EINVAL, "states_per_wave must be 0, 2, 4 or 8 (got %d)", S_req);
+  if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4)
+    return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", S_req);
   if (chunk_req < 0 || chunk_req % 64 != 0) return fail(SSM_EINVAL, "chunk must be 0 or a positive multiple of 64");
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, last_state};
   for (const void* q : ptrs)
@@ -155,9 +149,6 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   choose(batch, dim, dstate, L, &pl, &S, &chunk);
   if (plan != SSM_PLAN_AUTO) pl = plan;
   if (S_req) S = S_req;
-  if (S > 2 && !sg_instantiated(S, groups_for(dstate, S))) S = 2;
-  const int G = groups_for(dstate, S);
-  if (!sg_instantiated(S, G)) return fail(SSM_EUNSUPPORTED, "no kernel for %d states per wave x %d waves", S, G);
   if (pl == SSM_PLAN_TWOPASS) {
     if (chunk_req)
       chunk = chunk_req;
@@ -175,7 +166,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
 
   if (pl == SSM_PLAN_CARRY) {
     a.chunk = L;
-    hipError_t e = ssm::launch_cs_full(a, bf16, S, G, 1, st);
+    hipError_t e = ssm::launch_rows_full(a, bf16, S, 1, st);
     if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
     return SSM_OK;
   }
@@ -195,13 +186,13 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   a.chunk = chunk;
   a.agg_p = agg_p;
   a.agg_h = agg_h;
-  e = ssm::launch_cs_agg(a, bf16, S, G, K - 1, st);
+  e = ssm::launch_rows_agg(a, bf16, S, K - 1, st);
   if (e == hipSuccess) e = ssm::launch_combine(agg_p, agg_h, h_init, rows, K, st);
   if (e == hipSuccess) {
     a.agg_p = nullptr;
     a.agg_h = nullptr;
     a.h_init = h_init;
-    e = ssm::launch_cs_full(a, bf16, S, G, K, st);
+    e = ssm::launch_rows_full(a, bf16, S, K, st);
   }
   hipError_t ef = hipFreeAsync(ws, st);
   if (e != hipSuccess) return hip_fail(e, "two-pass launch");
@@ -223,17 +214,17 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const void* B, const void* C,
                       const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
                       float* last_state, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
-                      int plan, int states_per_wave, int64_t chunk, void* stream) {
+                      int plan, int states_per_lane, int64_t chunk, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, last_state, batch, d_inner, d_state,
-                       L, dtype, plan, states_per_wave, chunk, stream);
+                       L, dtype, plan, states_per_lane, chunk, stream);
 }
 
 int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int* plan,
-                      int* states_per_wave, int64_t* chunk) {
+                      int* states_per_lane, int64_t* chunk) {
   g_err.clear();
   if (int rc = check_sizes(batch, d_inner, d_state, L)) return rc;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
-  choose(batch, d_inner, d_state, L, plan, states_per_wave, chunk);
+  choose(batch, d_inner, d_state, L, plan, states_per_lane, chunk);
   return SSM_OK;
 }
 

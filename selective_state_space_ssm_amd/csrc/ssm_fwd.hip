@@ -8,27 +8,41 @@
 //
 // What runs where
 // ---------------
-// One workgroup owns 64 channels (one per lane) of one batch row and G
-// wavefronts; wavefront g carries states [g*S, g*S+S) of every channel, so a
-// lane holds S states of the recurrence h_n = a_n h_n + b_n in registers and
-// never writes h or the pairs (a, b) to memory ([Scan page] §2.2, the
-// channel-parallel, time-serial mapping, and §2.3 on fusing the
-// discretisation into the scan; [Mamba-2 page] §3-§4).
+// A workgroup owns 16 channels of one batch row and all (up to 16) states of
+// them.  Its W = 4/S wavefronts are split into rows of 16 lanes: lane `col`
+// of a row is channel c0 + col, and row `row` of wave `w` carries the S
+// states n = (4w + row)*S + s of that channel.  The recurrence
+// h_n = a_n h_n + b_n therefore runs time-serially in registers, one
+// (channel, state) chain per lane slot, and neither h nor the pairs (a, b)
+// are written to memory ([Scan page] §2.2, the channel-parallel,
+// time-serial mapping, and §2.3 on fusing the discretisation into the scan;
+// [Mamba-2 page] §3-§4).  Sixteen channels per workgroup (not 64) give
+// batch*d_inner/16 workgroups, enough for every CU of the chip at the
+// 130m-like shape (768 workgroups, three per CU, three waves per SIMD with
+// one state per lane), and S trades lanes for registers where channels are
+// plentiful.
 //
-// Time is processed in tiles of TT steps.  Per tile:
-//   prep  (all waves): coalesced vector loads of u, delta (and z) along L,
-//         Delta = softplus(delta + bias) kept in log2 units, Delta*u; both
-//         go to LDS.  The loads of the next tile are issued before the
-//         recurrence of this one, so HBM latency overlaps compute.
-//   recur (wave g):   a = exp2(Delta2 * A[d,n]), b = (Delta*u) * B[n,t],
-//         h = fma(a, h, b), partial y += C[n,t] * h over the wave's states.
-//         B and C are the same for all 64 lanes: they are read with scalar
-//         loads into SGPRs and used as the scalar operand of v_mul / v_fmac,
-//         so the shared [b, n, L] rows cost neither VGPRs nor LDS bandwidth.
-//   epi   (all waves): y = sum of the G partial sums + D*u, times silu(z),
-//         rounded to the storage type, coalesced vector stores.
+// Time is processed in tiles of kTT steps, with two barriers per tile:
+//   recur (every lane): a = exp2(Delta2 * A[d,n]), b = (Delta*u) * B[n,t],
+//         h = fma(a, h, b), partial y = sum over the lane's S states of
+//         C[n,t] * h, written to LDS per (row group, channel, step).
+//         B and C of step t for the row's state sit in one VGPR (lane j of
+//         the row holds step j of a 16-step half tile) and reach the whole
+//         row through DPP row_newbcast as an operand of v_mul / v_fmac.
+//   epi   (every thread, V steps of one channel): y = sum of the 4W partial
+//         sums + D*u, times silu(z); rounded to the storage type, stored.
+//   prep  (every thread, V steps of one channel, next tile): Delta2 =
+//         softplus(delta + bias) in log2 units and Delta*u into LDS; B and C
+//         of the tile (float32) into LDS.  The global loads of the tile
+//         after are issued right after, so they have a whole tile of
+//         recurrence to arrive.
 // Exp is v_exp_f32 (2^x): A is used unscaled because Delta is kept as
 // Delta2 = Delta*log2(e); Delta*u is formed from Delta2*ln(2).
+//
+// Steps past the end of the chunk (ragged last tile) and channels or states
+// past the problem size get Delta2 = 0, Delta*u = 0 and B = C = 0: the
+// identity step (a = 1, b = 0) of [Scan page] §2.1, so the registers need
+// no masking and only the stores are guarded.
 //
 // Modes (template MODE):
 //   kFull: start from zero or from a per-chunk start state, emit y over
@@ -52,22 +66,42 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTT = 32;          // steps per tile
-constexpr int kCH = 64;          // channels per workgroup (= lanes)
-constexpr int kRow = kTT + 4;    // LDS row stride in floats (conflict-free b128)
-constexpr int kQ4 = kTT / 4;     // 4-step groups per tile row
-constexpr int kSlots = kCH * kQ4;
+constexpr int kCG = 16;          // channels per workgroup (= lanes per row)
+constexpr int kNS = 16;          // state slots per workgroup (d_state <= 16)
+constexpr int kRow = kTT + 4;    // LDS row stride in floats (float4 rows, staggered banks)
 
 // ---------------------------------------------------------------- storage
+// Loads and stores of V consecutive elements (V = 1, 2, 4 or 8) of the
+// storage type, converted to / from float32.
 struct F32 {
   using T = float;
-  static __device__ __forceinline__ float4 ld4(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
+  template <int V>
+  static __device__ __forceinline__ void ld(const float* p, float* o) {
+    if constexpr (V == 1) {
+      o[0] = *p;
+    } else if constexpr (V == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      o[0] = v.x; o[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(p + i);
+        o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+      }
+    }
   }
-  static __device__ __forceinline__ float ld1(const float* p) { return *p; }
-  static __device__ __forceinline__ void st4(float* p, float4 v) {
-    *reinterpret_cast<float4*>(p) = v;
+  template <int V>
+  static __device__ __forceinline__ void st(float* p, const float* v) {
+    if constexpr (V == 1) {
+      *p = v[0];
+    } else if constexpr (V == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 4)
+        *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    }
   }
-  static __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -75,30 +109,189 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 struct BF16 {
   using T = uint16_t;
-  static __device__ __forceinline__ float4 ld4(const uint16_t* p) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    return make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+  static __device__ __forceinline__ uint32_t cvt(float f) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));  // RNE
   }
-  static __device__ __forceinline__ float ld1(const uint16_t* p) {
-    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  template <int V>
+  static __device__ __forceinline__ void ld(const uint16_t* p, float* o) {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    } else if constexpr (V == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      o[0] = bf_lo(w); o[1] = bf_hi(w);
+    } else if constexpr (V == 4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+      o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
+    }
   }
-  static __device__ __forceinline__ uint16_t cvt(float f) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt_pk_bf16_f32, RNE
+  template <int V>
+  static __device__ __forceinline__ void st(uint16_t* p, const float* v) {
+    if constexpr (V == 1) {
+      *p = static_cast<uint16_t>(cvt(v[0]));
+    } else if constexpr (V == 2) {
+      *reinterpret_cast<uint32_t*>(p) = cvt(v[0]) | (cvt(v[1]) << 16);
+    } else if constexpr (V == 4) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(cvt(v[0]) | (cvt(v[1]) << 16), cvt(v[2]) | (cvt(v[3]) << 16));
+    } else {
+      *reinterpret_cast<uint4*>(p) =
+          make_uint4(cvt(v[0]) | (cvt(v[1]) << 16), cvt(v[2]) | (cvt(v[3]) << 16),
+                     cvt(v[4]) | (cvt(v[5]) << 16), cvt(v[6]) | (cvt(v[7]) << 16));
+    }
   }
-  static __device__ __forceinline__ void st4(uint16_t* p, float4 v) {
-    uint2 w;
-    w.x = static_cast<uint32_t>(cvt(v.x)) | (static_cast<uint32_t>(cvt(v.y)) << 16);
-    w.y = static_cast<uint32_t>(cvt(v.z)) | (static_cast<uint32_t>(cvt(v.w)) << 16);
-    *reinterpret_cast<uint2*>(p) = w;
-  }
-  static __device__ __forceinline__ void st1(uint16_t* p, float v) { *p = cvt(v); }
 };
+
+// Buffer-resource access (raw buffer loads and stores).  A resource holds
+// a base address and a byte size in SGPRs; every access gives a 32-bit byte
+// offset, and a read past the size returns zero while a write past it is
+// dropped, so no address is ever clamped or masked in VGPRs.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 family: 32-bit untyped data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+
+struct BufF32 {
+  // raw 32-bit words of V elements, and their conversion to float32
+  template <int V>
+  static constexpr int kWords = V;
+  template <int V>
+  static __device__ __forceinline__ void ldw(Rsrc r, uint32_t off, uint32_t* w) {
+    if constexpr (V == 1) {
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (V == 2) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+      }
+    }
+  }
+  template <int V>
+  static __device__ __forceinline__ void unpack(const uint32_t* w, float* o) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = __uint_as_float(w[e]);
+  }
+  template <int V>
+  static __device__ __forceinline__ void ld(Rsrc r, uint32_t off, float* o) {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    } else if constexpr (V == 2) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      o[0] = __uint_as_float(w.x); o[1] = __uint_as_float(w.y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        o[i] = __uint_as_float(w.x); o[i + 1] = __uint_as_float(w.y);
+        o[i + 2] = __uint_as_float(w.z); o[i + 3] = __uint_as_float(w.w);
+      }
+    }
+  }
+  template <int V>
+  static __device__ __forceinline__ void st(Rsrc r, uint32_t off, const float* v) {
+    if constexpr (V == 1) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 0);
+    } else if constexpr (V == 2) {
+      u32x2 w;
+      w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        u32x4 w;
+        w.x = __float_as_uint(v[i]); w.y = __float_as_uint(v[i + 1]);
+        w.z = __float_as_uint(v[i + 2]); w.w = __float_as_uint(v[i + 3]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + 4 * i, 0, 0);
+      }
+    }
+  }
+};
+
+struct BufBF16 {
+  template <int V>
+  static constexpr int kWords = (V + 1) / 2;
+  template <int V>
+  static __device__ __forceinline__ void ldw(Rsrc r, uint32_t off, uint32_t* w) {
+    if constexpr (V == 1) {
+      w[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16;
+    } else if constexpr (V == 2) {
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (V == 4) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      w[0] = x.x; w[1] = x.y;
+    } else {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    }
+  }
+  // V == 1 words hold the element in their high half already
+  template <int V>
+  static __device__ __forceinline__ void unpack(const uint32_t* w, float* o) {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(w[0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; e += 2) {
+        o[e] = bf_lo(w[e / 2]);
+        o[e + 1] = bf_hi(w[e / 2]);
+      }
+    }
+  }
+  template <int V>
+  static __device__ __forceinline__ void ld(Rsrc r, uint32_t off, float* o) {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+    } else if constexpr (V == 2) {
+      const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      o[0] = bf_lo(w); o[1] = bf_hi(w);
+    } else if constexpr (V == 4) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+    } else {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+      o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
+    }
+  }
+  template <int V>
+  static __device__ __forceinline__ void st(Rsrc r, uint32_t off, const float* v) {
+    if constexpr (V == 1) {
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(BF16::cvt(v[0])), r, off, 0, 0);
+    } else if constexpr (V == 2) {
+      __builtin_amdgcn_raw_buffer_store_b32(BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16), r, off, 0, 0);
+    } else if constexpr (V == 4) {
+      u32x2 w;
+      w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
+      w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    } else {
+      u32x4 w;
+      w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
+      w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+      w.z = BF16::cvt(v[4]) | (BF16::cvt(v[5]) << 16);
+      w.w = BF16::cvt(v[6]) | (BF16::cvt(v[7]) << 16);
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+    }
+  }
+};
+
+template <typename IO> struct BufOf;
+template <> struct BufOf<F32> { using type = BufF32; };
+template <> struct BufOf<BF16> { using type = BufBF16; };
 
 __device__ __forceinline__ float get(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ void set(float4& v, int j, float x) {
-  if (j == 0) v.x = x; else if (j == 1) v.y = x; else if (j == 2) v.z = x; else v.w = x;
 }
 
 // Delta in log2 units from raw delta: x2 = (delta + bias) * log2(e);
@@ -121,17 +314,16 @@ __device__ __forceinline__ float silu(float zz) {
 
 // --------------------------------------------------------------------------
 // Broadcast of one step's B or C value: B and C for 16 consecutive steps sit
-// in one VGPR, lane j of every row of 16 lanes holding step j.  DPP
-// row_newbcast:j (gfx90a and later) hands lane j's value to its whole row as
-// the src0 operand of the consuming v_mul / v_fmac, at no extra instruction.
+// in one VGPR, lane j of every row of 16 lanes holding step j of that row's
+// state.  DPP row_newbcast:j (gfx90a and later) hands lane j's value to its
+// whole row as the src0 operand of the consuming v_mul / v_fmac, at no extra
+// instruction.  Written out as inline asm so that every mode gets the fused
+// form (the compiler folds a separate broadcast into v_mul only when both
+// sit in one basic block, and never into v_fmac).  Hazard: a DPP source
+// must not have been written by a VALU instruction in the two preceding
+// instructions; c is only ever written by LDS loads, which
+// tests/test_isa_hazards.py checks on the generated ISA.
 // --------------------------------------------------------------------------
-// x * bcast16<J>(c) and acc += bcast16<J>(c) * h as single v_mul_f32_dpp /
-// v_fmac_f32_dpp instructions, written out so that every mode gets the fused
-// form (the compiler folds a separate broadcast into v_mul only when both sit
-// in one basic block, and never into v_fmac).  Hazard: a DPP source must not
-// have been written by a VALU instruction in the two preceding instructions;
-// c is only ever written by memory loads, which tests/test_isa_hazards.py
-// checks on the generated ISA.
 template <int J>
 __device__ __forceinline__ float mul_bcast16(float c, float x) {
   float r;
@@ -157,322 +349,388 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // --------------------------------------------------------------------------
-// Channel-serial kernel.  Template: storage IO, states per wave S, waves G,
-// mode, and GATED (z present).  Grid: x = channel block (64 channels),
-// y = batch row, z = chunk.  Every pointer is a separate __restrict__
-// parameter: the caller guarantees that outputs overlap no input.
-//
-// Two code paths share the registers and LDS layout:
-//  * fast: a full block of 64 channels, whole tiles, L % 4 == 0.  The loop
-//    body is straight-line (next-tile prefetches use clamped addresses
-//    instead of branches), so the compiler can count outstanding memory
-//    operations exactly and wait only for the ones each step consumes.
-//  * generic: any tail tile, a partial channel block or unaligned L; loads
-//    and stores element by element with bounds checks, no prefetch.
+// Row-layout kernel.  Template: storage IO, states per lane S (1, 2, 4),
+// mode, GATED (z present), VEC (L is a multiple of 8: vector loads and
+// stores).  Grid: x = channel group (16 channels), y = batch row,
+// z = chunk.  Block: 64 * (4 / S) threads.  Every pointer is
+// a separate __restrict__ parameter: the caller guarantees that outputs
+// overlap no input.
 // --------------------------------------------------------------------------
-template <typename IO, int S, int G, int MODE, bool GATED>
-__global__ __launch_bounds__(64 * G) void ssm_cs_kernel(
+template <typename IO, int S, int MODE, bool GATED, bool VEC>
+__global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(
     const typename IO::T* __restrict__ u, const typename IO::T* __restrict__ dlt,
     const float* __restrict__ Ag, const typename IO::T* __restrict__ Bg, const typename IO::T* __restrict__ Cg,
     const float* __restrict__ Dg, const typename IO::T* __restrict__ zg, const float* __restrict__ biasg,
     typename IO::T* __restrict__ yg, float* __restrict__ last_state, const float* __restrict__ h_init,
     float* __restrict__ agg_p, float* __restrict__ agg_h, CsSizes p) {
   using T = typename IO::T;
-  constexpr int kThreads = 64 * G;
-  constexpr int kSPT = (kSlots + kThreads - 1) / kThreads;  // prep/epilogue slots per thread
-  constexpr bool kEvenSlots = (kSlots % kThreads) == 0;
-  constexpr int kH = kTT / 16;                               // 16-step halves per tile
+  constexpr int W = 4 / S;                 // wavefronts
+  constexpr int NT = 64 * W;               // threads
+  constexpr int NG = 4 * W;                // partial-sum groups (rows of all waves)
+  constexpr int V = kCG * kTT / NT;        // prep / epilogue steps per thread
+  constexpr int TPC = kTT / V;             // prep / epilogue threads per channel
+  constexpr int BCQ = 2 * kNS * kTT / 4 / NT;  // B/C float4 groups per thread
   constexpr bool kGate = GATED && MODE == kFull;
-  constexpr int kNS = S * G;                                 // state rows staged per tile
-  constexpr int kBCq = 2 * kNS * kQ4;                        // 4-step B/C groups per tile
-  constexpr int kBCPT = (kBCq + kThreads - 1) / kThreads;    // ... per thread
+  static_assert(S == 1 || S == 2 || S == 4, "S");
+  static_assert(V * NT == kCG * kTT && BCQ * NT * 4 == 2 * kNS * kTT, "tiling");
 
   extern __shared__ float smem[];
-  float* sDt = smem;                 // [64][kRow]  Delta2
-  float* sDu = sDt + kCH * kRow;     // [64][kRow]  Delta * u
-  float* sBC = sDu + kCH * kRow;     // [2][kNS][kTT] B and C of the tile, float32 (fast path)
-  float* sY = sBC + 2 * kNS * kTT;   // [G][64][kRow] partial y (kFull only)
+  float* sDt = smem;                  // [16][kRow]  Delta2
+  float* sDu = sDt + kCG * kRow;      // [16][kRow]  Delta * u
+  float* sBC = sDu + kCG * kRow;      // [2][16][kTT] B rows, then C rows (float32)
+  float* sP = sBC + 2 * kNS * kTT;    // [NG][16][kRow] partial y (kFull only)
 
   const int tid = threadIdx.x;
   // the wave index as an SGPR keeps every per-wave quantity uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int row = lane >> 4;
+  const int col = lane & 15;
   const int64_t dim = p.dim, L = p.L, N = p.dstate;
-  const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kCH;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kCG;
   const int64_t b = blockIdx.y;
   const int64_t k = blockIdx.z;
-  const int64_t t_begin = k * p.chunk;
-  const int64_t t_end = (t_begin + p.chunk < L) ? t_begin + p.chunk : L;
+  // time indices fit in 32 bits (the host rejects L >= 2^31)
+  const int Li = static_cast<int>(L);
+  const int t_begin = static_cast<int>(k * p.chunk);
+  const int t_end = (p.chunk < Li - t_begin) ? t_begin + static_cast<int>(p.chunk) : Li;
   const bool softplus = p.softplus != 0;
 
-  // ---- recurrence registers: S states of channel d0 + lane
-  const int64_t d = d0 + lane;
+  // ---- recurrence registers: S states of channel c0 + col
+  const int grp = wave * 4 + row;
+  const int64_t d = c0 + col;
   const bool dvalid = d < dim;
   float h[S], An[S];
-  const T* Brow[S];
-  const T* Crow[S];
-  bool svalid[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int64_t n = static_cast<int64_t>(wave) * S + s;
-    svalid[s] = n < N;                                   // uniform per wave
-    const int64_t nn = svalid[s] ? n : 0;
-    An[s] = (svalid[s] && dvalid) ? Ag[d * N + nn] : 0.0f;
+    const int64_t n = static_cast<int64_t>(grp) * S + s;
+    const bool ok = dvalid && n < N;
+    An[s] = ok ? Ag[d * N + n] : 0.0f;
     h[s] = 0.0f;
-    if (MODE == kFull && h_init != nullptr && svalid[s] && dvalid)
-      h[s] = h_init[((k * p.batch + b) * N + nn) * dim + d];
-    Brow[s] = Bg + (b * N + nn) * L;
-    Crow[s] = Cg + (b * N + nn) * L;
+    if (MODE == kFull && h_init != nullptr && ok) h[s] = h_init[((k * p.batch + b) * N + n) * dim + d];
   }
   float dsum = 0.0f;  // kAgg: sum of Delta2 over the chunk
 
-  // ---- prep/epilogue slots of this thread: (row, 4-step group)
-  float bias2[kSPT], Dd[kSPT];
+  // ---- prep / epilogue slot of this thread: channel pc, steps [pt, pt + V)
+  using Buf = typename BufOf<IO>::type;
+  constexpr uint32_t ES = sizeof(T);
+  const int pc = tid / TPC;
+  const int pt = (tid % TPC) * V;
+  const int64_t pd = c0 + pc;
+  const bool pvalid = pd < dim;
+  const float bias2 = (pvalid && biasg != nullptr) ? biasg[pd] * kLog2e : 0.0f;
+  const float Dd = (pvalid && Dg != nullptr) ? Dg[pd] : 0.0f;
+
+  // Buffer resources over this workgroup's rows of u, delta, z, y (its
+  // channels of batch row b) and over batch row b of B and C.  Channels
+  // past d_inner and states past d_state lie past the resource's size: they
+  // read as zero and their writes are dropped.  Byte offsets fit in 32 bits
+  // (the host bounds 16 * L * element size).
+  const int64_t rows_here = (dim - c0 < kCG) ? dim - c0 : kCG;
+  const int64_t row0 = (b * dim + c0) * L;
+  const uint32_t in_bytes = static_cast<uint32_t>(rows_here * L * ES);
+  const Rsrc rU = make_rsrc(u + row0, in_bytes);
+  const Rsrc rD = make_rsrc(dlt + row0, in_bytes);
+  const Rsrc rZ = make_rsrc(kGate ? zg + row0 : u + row0, in_bytes);
+  const Rsrc rY = make_rsrc(MODE == kFull ? yg + row0 : u + row0, in_bytes);
+  const uint32_t bc_bytes = static_cast<uint32_t>(N * L * ES);
+  const Rsrc rB = make_rsrc(Bg + b * N * L, bc_bytes);
+  const Rsrc rC = make_rsrc(Cg + b * N * L, bc_bytes);
+  const uint32_t poff = static_cast<uint32_t>((pc * L + pt) * ES);
+
+  // B/C slots of this thread: group q = tid + i*NT covers 4 steps of state n
+  // of B (first 128 groups) or C; the tensor is the same for a whole wave.
+  uint32_t bcoff[BCQ];
+  bool bcis_c[BCQ];
 #pragma unroll
-  for (int j = 0; j < kSPT; ++j) {
-    const int q = tid + j * kThreads;
-    const int64_t dd = d0 + q / kQ4;
-    const bool ok = q < kSlots && dd < dim;
-    bias2[j] = (ok && biasg) ? biasg[dd] * kLog2e : 0.0f;
-    Dd[j] = (ok && Dg) ? Dg[dd] : 0.0f;
+  for (int i = 0; i < BCQ; ++i) {
+    const int q = tid + i * NT;
+    bcis_c[i] = __builtin_amdgcn_readfirstlane((wave * 64 + i * NT) / (kNS * kTT / 4)) != 0;
+    const int n = (q / (kTT / 4)) % kNS;
+    bcoff[i] = static_cast<uint32_t>((n * L + (q % (kTT / 4)) * 4) * ES);
   }
 
-  const float* rowDt = sDt + lane * kRow;
-  const float* rowDu = sDu + lane * kRow;
-  float* rowY = sY + (wave * kCH + lane) * kRow;
+  // Raw inputs of one tile (32-bit words as loaded), a whole tile of
+  // recurrence ahead of use.  The loads are straight-line code (reads past a
+  // row run into the next row or past the resource, both harmless); prep
+  // pins the words, converts them and zeroes whatever lies past the chunk,
+  // so nothing touches a loaded register before prep.
+  // words per tile row slice and per B/C group: packed (VEC) or one per element
+  constexpr int RW = VEC ? Buf::template kWords<V> : V;
+  constexpr int BW = VEC ? Buf::template kWords<4> : 4;
+  struct TileRegs {
+    uint32_t wu[RW], wd[RW], wz[RW];
+    uint32_t wbc[BCQ][BW];
+    int t0;  // first step of the tile the words hold
+  };
 
-  // Reduce the G partial sums of one slot, add D*u, gate, store (fast path).
-  auto epilogue_slot = [&](int j, int64_t t0, float4 uu, float4 zz, bool vec) {
-    const int q = tid + j * kThreads;
-    const int r = q / kQ4;
-    const int c4 = (q % kQ4) * 4;
-    float4 acc = *reinterpret_cast<const float4*>(sY + r * kRow + c4);
+  auto load_tile = [&](TileRegs& R, int t0) {
+    uint32_t* wu = R.wu;
+    uint32_t* wd = R.wd;
+    uint32_t* wz = R.wz;
+    auto& wbc = R.wbc;
+    R.t0 = t0;
+    if (!kGate) {
 #pragma unroll
-    for (int g = 1; g < G; ++g) {
-      const float4 v = *reinterpret_cast<const float4*>(sY + (g * kCH + r) * kRow + c4);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      for (int e = 0; e < RW; ++e) wz[e] = 0u;
     }
-    float4 out;
+    const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if constexpr (VEC) {
+      Buf::template ldw<V>(rU, poff + toff, wu);
+      Buf::template ldw<V>(rD, poff + toff, wd);
+      if (kGate) Buf::template ldw<V>(rZ, poff + toff, wz);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float yv = __builtin_fmaf(Dd[j], get(uu, e), get(acc, e));
-      if (kGate) yv = yv * silu(get(zz, e));
-      set(out, e, yv);
-    }
-    const int64_t dd = d0 + r;
-    const int64_t t = t0 + c4;
-    const int64_t off = (b * dim + dd) * L + t;
-    if (vec) {
-      IO::st4(yg + off, out);
-    } else if (dd < dim) {
+      for (int i = 0; i < BCQ; ++i) Buf::template ldw<4>(bcis_c[i] ? rC : rB, bcoff[i] + toff, wbc[i]);
+    } else {
+      // one element per load; the words then hold float32 bits (F32) or a
+      // bfloat16 in their high half (BF16), as ldw<1> returns them
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (t + e < t_end) IO::st1(yg + off + e, get(out, e));
+      for (int e = 0; e < V; ++e) {
+        Buf::template ldw<1>(rU, poff + toff + e * ES, &wu[e]);
+        Buf::template ldw<1>(rD, poff + toff + e * ES, &wd[e]);
+        if (kGate) Buf::template ldw<1>(rZ, poff + toff + e * ES, &wz[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < BCQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Buf::template ldw<1>(bcis_c[i] ? rC : rB, bcoff[i] + toff + e * ES, &wbc[i][e]);
     }
   };
 
-  // ======================== fast path ========================
-  const bool fast = (L % 4 == 0) && (d0 + kCH <= dim) && kEvenSlots;
-  const int64_t n_fast = fast ? (t_end - t_begin) / kTT : 0;
-  const int64_t t_fast_end = t_begin + n_fast * kTT;
-  if (n_fast > 0) {
-    // raw inputs of the next tile, prefetched one tile ahead
-    float4 ru[kSPT], rd[kSPT], rz[kSPT], rbc[kBCPT];
-    auto fetch = [&](int64_t t0) {
+  // Convert the pinned words of the tile to float32.
+  float ru[V], rd[V], rz[V];
+  float4 rbc[BCQ];
+  auto unpack_tile = [&](TileRegs& R) {
+    uint32_t* wu = R.wu;
+    uint32_t* wd = R.wd;
+    uint32_t* wz = R.wz;
+    auto& wbc = R.wbc;
 #pragma unroll
-      for (int j = 0; j < kSPT; ++j) {
-        const int q = tid + j * kThreads;
-        const int64_t off = (b * dim + d0 + q / kQ4) * L + t0 + (q % kQ4) * 4;
-        ru[j] = IO::ld4(u + off);
-        rd[j] = IO::ld4(dlt + off);
-        if (kGate) rz[j] = IO::ld4(zg + off);
+    for (int e = 0; e < RW; ++e) asm volatile("" : "+v"(wu[e]), "+v"(wd[e]), "+v"(wz[e]));
+#pragma unroll
+    for (int i = 0; i < BCQ; ++i)
+#pragma unroll
+      for (int e = 0; e < BW; ++e) asm volatile("" : "+v"(wbc[i][e]));
+    if constexpr (VEC) {
+      Buf::template unpack<V>(wu, ru);
+      Buf::template unpack<V>(wd, rd);
+      Buf::template unpack<V>(wz, rz);
+#pragma unroll
+      for (int i = 0; i < BCQ; ++i) {
+        float v[4];
+        Buf::template unpack<4>(wbc[i], v);
+        rbc[i] = make_float4(v[0], v[1], v[2], v[3]);
       }
-      // B then C rows of every staged state; rows past d_state read row 0
-      // and are zeroed when written to LDS.  Every thread issues its loads
-      // (surplus threads re-read a valid group) so that the number of memory
-      // operations in flight is the same on every path.
+    } else {
 #pragma unroll
-      for (int j = 0; j < kBCPT; ++j) {
-        const int q = (tid + j * kThreads) % kBCq;
-        const int row = q / kQ4;                    // 0..2*kNS-1
-        const int n = row % kNS;
-        const T* base = (row < kNS) ? Bg : Cg;
-        const int64_t nn = (n < N) ? n : 0;
-        rbc[j] = IO::ld4(base + (b * N + nn) * L + t0 + (q % kQ4) * 4);
+      for (int e = 0; e < V; ++e) {
+        Buf::template unpack<1>(&wu[e], &ru[e]);
+        Buf::template unpack<1>(&wd[e], &rd[e]);
+        Buf::template unpack<1>(&wz[e], &rz[e]);
       }
-    };
-
-    float4 pu[kSPT], pz[kSPT];  // u, z of the tile whose epilogue is pending
-
-    // ---- prep: Delta2, Delta*u, B, C of the tile in registers into LDS
-    auto prep = [&]() {
 #pragma unroll
-      for (int j = 0; j < kSPT; ++j) {
-        const int q = tid + j * kThreads;
-        const int r = q / kQ4;
-        const int c4 = (q % kQ4) * 4;
-        float4 dt, du;
+      for (int i = 0; i < BCQ; ++i) {
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v2 = delta2(get(rd[j], e), bias2[j], softplus);
-          set(dt, e, v2);
-          set(du, e, (v2 * kLn2) * get(ru[j], e));
+        for (int e = 0; e < 4; ++e) Buf::template unpack<1>(&wbc[i][e], &v[e]);
+        rbc[i] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  };
+
+  // D*u and silu(z) of the tile just prepared (n*) and of the tile whose
+  // epilogue is pending (c*).  Prep computes them from the loaded registers,
+  // so no loaded value is ever copied: a copy would let the compiler keep the
+  // next tile's load in another register and wait for it at the loop's end.
+  float nDu[V], nG[V];
+  float cDu[V], cG[V];
+
+  // ---- prep: Delta2, Delta*u, B, C of the tile held in registers into LDS.
+  // In the ragged last tile, steps past the chunk become identity steps
+  // (Delta2 = Delta*u = 0, B = C = 0).  Channels past d_inner read u = 0
+  // (so Delta*u = 0) and their lanes have A = 0 (so a = 1): their state
+  // stays zero without a mask.
+  // Pin nDu / nG into VGPRs where prep computes them, so the compiler cannot
+  // sink their products past the next load of the same registers.
+  auto pin = [&]() {
+#pragma unroll
+    for (int e = 0; e < V; ++e) asm volatile("" : "+v"(nDu[e]), "+v"(nG[e]));
+  };
+  auto prep = [&](TileRegs& R) {
+    unpack_tile(R);
+    const int r_t0 = R.t0;
+    float dt[V], du[V];
+    if (r_t0 + kTT <= t_end) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float v2 = delta2(rd[e], bias2, softplus);
+        dt[e] = v2;
+        du[e] = (v2 * kLn2) * ru[e];
+        nDu[e] = Dd * ru[e];
+        nG[e] = kGate ? silu(rz[e]) : 1.0f;
+      }
+      pin();
+      F32::template st<V>(sDt + pc * kRow + pt, dt);
+      F32::template st<V>(sDu + pc * kRow + pt, du);
+#pragma unroll
+      for (int i = 0; i < BCQ; ++i) *reinterpret_cast<float4*>(sBC + (tid + i * NT) * 4) = rbc[i];
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const bool ok = r_t0 + pt + e < t_end;
+        const float uu = ok ? ru[e] : 0.0f;
+        const float v2 = ok ? delta2(rd[e], bias2, softplus) : 0.0f;
+        dt[e] = v2;
+        du[e] = (v2 * kLn2) * uu;
+        nDu[e] = Dd * uu;
+        nG[e] = (kGate && ok) ? silu(rz[e]) : 1.0f;
+      }
+      pin();
+      F32::template st<V>(sDt + pc * kRow + pt, dt);
+      F32::template st<V>(sDu + pc * kRow + pt, du);
+#pragma unroll
+      for (int i = 0; i < BCQ; ++i) {
+        const int q = tid + i * NT;
+        const int t = r_t0 + (q % (kTT / 4)) * 4;
+        float4 v = rbc[i];
+        v.x = t < t_end ? v.x : 0.0f;
+        v.y = t + 1 < t_end ? v.y : 0.0f;
+        v.z = t + 2 < t_end ? v.z : 0.0f;
+        v.w = t + 3 < t_end ? v.w : 0.0f;
+        *reinterpret_cast<float4*>(sBC + q * 4) = v;
+      }
+    }
+  };
+
+  // ---- recurrence of one tile from LDS
+  const float* rowDt = sDt + col * kRow;
+  const float* rowDu = sDu + col * kRow;
+  float* rowP = sP + (grp * kCG + col) * kRow;
+  auto recur = [&]() {
+    float bc[S][2], cc[S][2];  // lane j of the row: step 16*half + j of state grp*S+s
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int n = grp * S + s;
+        bc[s][hh] = sBC[n * kTT + 16 * hh + col];
+        cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + 16 * hh + col] : 0.0f;
+      }
+    static_for<0, 2>([&](auto HH) {
+      constexpr int hh = decltype(HH)::value;
+      float4 dq[4], uq[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        dq[g4] = *reinterpret_cast<const float4*>(rowDt + 16 * hh + g4 * 4);
+        uq[g4] = *reinterpret_cast<const float4*>(rowDu + 16 * hh + g4 * 4);
+      }
+      float y4[4];
+      static_for<0, 16>([&](auto JJ) {
+        constexpr int j = decltype(JJ)::value;
+        // The aggregate pass has no LDS store every four steps to bound how
+        // far the scheduler hoists the exps of later steps (it then runs out
+        // of registers): an empty asm that takes this group's Delta values
+        // and the state after the previous group orders the groups.
+        if constexpr (MODE == kAgg && j % 4 == 0) {
+          asm volatile("" : "+v"(dq[j / 4].x), "+v"(dq[j / 4].y), "+v"(dq[j / 4].z), "+v"(dq[j / 4].w));
+          asm volatile("" : "+v"(uq[j / 4].x), "+v"(uq[j / 4].y), "+v"(uq[j / 4].z), "+v"(uq[j / 4].w));
+#pragma unroll
+          for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
         }
-        *reinterpret_cast<float4*>(sDt + r * kRow + c4) = dt;
-        *reinterpret_cast<float4*>(sDu + r * kRow + c4) = du;
-        pu[j] = ru[j];
-        pz[j] = rz[j];
-      }
+        const float dt = get(dq[j / 4], j % 4);
+        const float du = get(uq[j / 4], j % 4);
+        float yv = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kBCPT; ++j) {
-        const int q = tid + j * kThreads;
-        if (kBCq % kThreads != 0 && q >= kBCq) continue;
-        const int row = q / kQ4;
-        const bool ok = (row % kNS) < N && (MODE == kFull || row < kNS);
-        *reinterpret_cast<float4*>(sBC + row * kTT + (q % kQ4) * 4) =
-            ok ? rbc[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    };
-
-    // ---- recurrence of one tile from LDS
-    auto recur = [&]() {
-      float4 dq[kQ4], uq[kQ4];
-      float bc[S][kH], cc[S][kH];  // lane l: step 16*half + (l & 15) of state wave*S+s
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int hh = 0; hh < kH; ++hh) {
-          const int n = wave * S + s;
-          bc[s][hh] = sBC[n * kTT + 16 * hh + (lane & 15)];
-          cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + 16 * hh + (lane & 15)] : 0.0f;
-        }
-#pragma unroll
-      for (int g4 = 0; g4 < kQ4; ++g4) {
-        dq[g4] = *reinterpret_cast<const float4*>(rowDt + g4 * 4);
-        uq[g4] = *reinterpret_cast<const float4*>(rowDu + g4 * 4);
-      }
-      static_for<0, kH>([&](auto HH) {
-        constexpr int hh = decltype(HH)::value;
-        float4 y4;
-        static_for<0, 16>([&](auto JJ) {
-          constexpr int j = decltype(JJ)::value;
-          constexpr int st = hh * 16 + j;
-          const float dt = get(dq[st / 4], st % 4);
-          const float du = get(uq[st / 4], st % 4);
-          float yv = 0.0f;
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const float a = __builtin_amdgcn_exp2f(dt * An[s]);
-            h[s] = __builtin_fmaf(a, h[s], mul_bcast16<j>(bc[s][hh], du));
-            if (MODE == kFull) {
-              if (s == 0)
-                yv = mul_bcast16<j>(cc[s][hh], h[s]);
-              else
-                fmac_bcast16<j>(yv, cc[s][hh], h[s]);
-            }
+        for (int s = 0; s < S; ++s) {
+          const float a = __builtin_amdgcn_exp2f(dt * An[s]);
+          h[s] = __builtin_fmaf(a, h[s], mul_bcast16<j>(bc[s][hh], du));
+          if (MODE == kFull) {
+            if (s == 0)
+              yv = mul_bcast16<j>(cc[s][hh], h[s]);
+            else
+              fmac_bcast16<j>(yv, cc[s][hh], h[s]);
           }
-          if (MODE == kAgg) dsum += dt;
-          set(y4, j % 4, yv);
-          if (MODE == kFull && j % 4 == 3) *reinterpret_cast<float4*>(rowY + st - 3) = y4;
-        });
+        }
+        if (MODE == kAgg) dsum += dt;
+        y4[j % 4] = yv;
+        if (MODE == kFull && j % 4 == 3)
+          *reinterpret_cast<float4*>(rowP + 16 * hh + j - 3) = make_float4(y4[0], y4[1], y4[2], y4[3]);
+
       });
-    };
+    });
+  };
 
-    auto epilogue = [&](int64_t t0) {
-      if (MODE == kFull) {
+  // ---- epilogue of the tile at t0: sum partials, D skip, gate, store
+  auto epilogue = [&](int t0) {
+    float acc[V];
+    F32::template ld<V>(sP + pc * kRow + pt, acc);
 #pragma unroll
-        for (int j = 0; j < kSPT; ++j) epilogue_slot(j, t0, pu[j], pz[j], true);
-      }
-    };
+    for (int gg = 1; gg < NG; ++gg) {
+      float v[V];
+      F32::template ld<V>(sP + (gg * kCG + pc) * kRow + pt, v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += v[e];
+    }
+    float out[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) out[e] = kGate ? (acc[e] + cDu[e]) * cG[e] : acc[e] + cDu[e];
+    const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if (VEC && t0 + kTT <= t_end) {
+      Buf::template st<V>(rY, poff + toff, out);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (t0 + pt + e < t_end) Buf::template st<1>(rY, poff + toff + e * ES, &out[e]);
+    }
+  };
 
-    // Tile 0 is peeled and every later iteration starts with the previous
-    // tile's epilogue: the loop is entered from both sides with the same
-    // memory operations outstanding (the prefetched loads are the newest),
-    // so waits are counted exactly and never include the y stores.
-    fetch(t_begin);
-    prep();
-    fetch(n_fast > 1 ? t_begin + kTT : t_begin);
-    __syncthreads();
+  // Per tile: recurrence | barrier | prep of the next tile, epilogue of this
+  // tile, loads of the tile two ahead | barrier.  Two register sets (A for
+  // even tiles, B for odd ones) keep two tiles of loads in flight, which the
+  // HBM latency under load needs; the loop is unrolled by two so each set
+  // stays in fixed registers.  Prep, epilogue and loads run unconditionally
+  // (past the chunk they read harmless words and prepare identity steps that
+  // nothing stores): a conditional load would make the compiler copy its
+  // result at the join and wait for it there.  An odd tile count runs one
+  // extra all-identity tile.
+  const int ntiles = (t_end - t_begin + kTT - 1) / kTT;
+  TileRegs A, B;
+  load_tile(A, t_begin);
+  load_tile(B, t_begin + kTT);
+  prep(A);
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    cDu[e] = nDu[e];
+    cG[e] = nG[e];
+  }
+  load_tile(A, t_begin + 2 * kTT);
+  __syncthreads();
+  auto half_step = [&](int t0, TileRegs& next, TileRegs& reload) {
     recur();
     __syncthreads();
-    for (int64_t it = 1; it < n_fast; ++it) {
-      const int64_t t0 = t_begin + it * kTT;
-      const int64_t tn = (it + 1 < n_fast) ? t0 + kTT : t0;
-      epilogue(t0 - kTT);
-      prep();
-      fetch(tn);
-      __syncthreads();
-      recur();
-      __syncthreads();
-    }
-    epilogue(t_fast_end - kTT);
-  }
-
-  // ======================== generic path ========================
-  for (int64_t t0 = t_fast_end; t0 < t_end; t0 += kTT) {
-    const int nsteps = static_cast<int>((t_end - t0 < kTT) ? (t_end - t0) : kTT);
-    float4 pu[kSPT], pz[kSPT];
+    prep(next);
+    if (MODE == kFull) epilogue(t0);
 #pragma unroll
-    for (int j = 0; j < kSPT; ++j) {
-      const int q = tid + j * kThreads;
-      pu[j] = pz[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (q >= kSlots) continue;
-      const int r = q / kQ4;
-      const int c4 = (q % kQ4) * 4;
-      const int64_t dd = d0 + r;
-      const int64_t t = t0 + c4;
-      float4 dt = make_float4(0.f, 0.f, 0.f, 0.f), du = dt;
-      if (dd < dim) {
-        const int64_t off = (b * dim + dd) * L + t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (t + e < t_end) {
-            const float uu = IO::ld1(u + off + e);
-            const float v2 = delta2(IO::ld1(dlt + off + e), bias2[j], softplus);
-            set(dt, e, v2);
-            set(du, e, (v2 * kLn2) * uu);
-            set(pu[j], e, uu);
-            if (kGate) set(pz[j], e, IO::ld1(zg + off + e));
-          }
-        }
-      }
-      *reinterpret_cast<float4*>(sDt + r * kRow + c4) = dt;
-      *reinterpret_cast<float4*>(sDu + r * kRow + c4) = du;
+    for (int e = 0; e < V; ++e) {
+      cDu[e] = nDu[e];
+      cG[e] = nG[e];
     }
+    load_tile(reload, t0 + 3 * kTT);
     __syncthreads();
-    for (int e = 0; e < nsteps; ++e) {
-      const float dt = rowDt[e], du = rowDu[e];
-      float yv = 0.0f;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const float bv = svalid[s] ? IO::ld1(Brow[s] + t0 + e) : 0.0f;
-        const float cv = (MODE == kFull && svalid[s]) ? IO::ld1(Crow[s] + t0 + e) : 0.0f;
-        const float a = __builtin_amdgcn_exp2f(dt * An[s]);
-        h[s] = __builtin_fmaf(a, h[s], du * bv);
-        if (MODE == kFull) yv = (s == 0) ? cv * h[s] : __builtin_fmaf(cv, h[s], yv);
-      }
-      if (MODE == kAgg) dsum += dt;
-      if (MODE == kFull) rowY[e] = yv;
-    }
-    __syncthreads();
-    if (MODE == kFull) {
-#pragma unroll
-      for (int j = 0; j < kSPT; ++j) {
-        const int q = tid + j * kThreads;
-        if (q >= kSlots) continue;
-        if (t0 + (q % kQ4) * 4 >= t_end) continue;
-        epilogue_slot(j, t0, pu[j], pz[j], false);
-      }
-    }
-    __syncthreads();
+  };
+#pragma unroll 1
+  for (int it = 0; it < ntiles; it += 2) {
+    const int t0 = t_begin + it * kTT;
+    half_step(t0, B, B);
+    half_step(t0 + kTT, A, A);
   }
 
   // ---- chunk end: final state or chunk aggregate
   if (!dvalid) return;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    if (!svalid[s]) continue;
-    const int64_t n = static_cast<int64_t>(wave) * S + s;
+    const int64_t n = static_cast<int64_t>(grp) * S + s;
+    if (n >= N) continue;
     if (MODE == kFull) {
       if (last_state != nullptr && t_end == L) last_state[(b * dim + d) * N + n] = h[s];
     } else {
@@ -505,54 +763,59 @@ __global__ __launch_bounds__(256) void ssm_combine_kernel(const float* __restric
 // --------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------
-size_t cs_smem_bytes(int S, int G, int mode) {
-  return sizeof(float) * (static_cast<size_t>(kCH) * kRow * (2 + (mode == kFull ? G : 0)) +
-                          static_cast<size_t>(2) * S * G * kTT);
+size_t rows_smem_bytes(int S, int mode) {
+  const int W = 4 / S;
+  return sizeof(float) * (static_cast<size_t>(2) * kCG * kRow + static_cast<size_t>(2) * kNS * kTT +
+                          (mode == kFull ? static_cast<size_t>(4 * W) * kCG * kRow : 0));
 }
 
-int cs_time_tile() { return kTT; }
+int rows_time_tile() { return kTT; }
 
-template <typename IO, int S, int G, int MODE, bool GATED>
-static hipError_t launch_cs_v(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
+template <typename IO, int S, int MODE, bool GATED, bool VEC>
+static hipError_t launch_rows_v(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
   using T = typename IO::T;
-  const dim3 grid(static_cast<unsigned>((a.dim + kCH - 1) / kCH), static_cast<unsigned>(a.batch),
+  const dim3 grid(static_cast<unsigned>((a.dim + kCG - 1) / kCG), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(nchunks));
-  const size_t smem = cs_smem_bytes(S, G, MODE);
-  auto kern = ssm_cs_kernel<IO, S, G, MODE, GATED>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(smem));
+  const size_t smem = rows_smem_bytes(S, MODE);
+  auto kern = ssm_rows_kernel<IO, S, MODE, GATED, VEC>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
   CsSizes sz;
   sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.chunk = a.chunk; sz.softplus = a.softplus;
-  hipLaunchKernelGGL(kern, grid, dim3(64 * G), smem, st, static_cast<const T*>(a.u), static_cast<const T*>(a.delta),
-                     a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.D, static_cast<const T*>(a.z),
-                     a.bias, static_cast<T*>(a.y), a.last_state, a.h_init, a.agg_p, a.agg_h, sz);
+  hipLaunchKernelGGL(kern, grid, dim3(256 / S), smem, st, static_cast<const T*>(a.u),
+                     static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
+                     a.D, static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.last_state, a.h_init,
+                     a.agg_p, a.agg_h, sz);
   return hipGetLastError();
 }
 
-template <typename IO, int S, int G, int MODE>
-static hipError_t launch_cs(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
-  if (MODE == kFull && a.z != nullptr) return launch_cs_v<IO, S, G, MODE, true>(a, nchunks, st);
-  return launch_cs_v<IO, S, G, MODE, false>(a, nchunks, st);
+template <typename IO, int S, int MODE>
+static hipError_t dispatch_flags(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
+  const bool vec = a.L % 8 == 0;
+  if constexpr (MODE == kFull) {
+    if (a.z != nullptr)
+      return vec ? launch_rows_v<IO, S, MODE, true, true>(a, nchunks, st)
+                 : launch_rows_v<IO, S, MODE, true, false>(a, nchunks, st);
+  }
+  return vec ? launch_rows_v<IO, S, MODE, false, true>(a, nchunks, st)
+             : launch_rows_v<IO, S, MODE, false, false>(a, nchunks, st);
 }
 
 template <typename IO, int MODE>
-static hipError_t dispatch_sg(const FwdArgs& a, int S, int G, int64_t nchunks, hipStream_t st) {
-#define SSM_CASE(SS, GG) \
-  if (S == SS && G == GG) return launch_cs<IO, SS, GG, MODE>(a, nchunks, st);
-  SSM_CASE(2, 1) SSM_CASE(2, 2) SSM_CASE(2, 4) SSM_CASE(2, 8)
-  SSM_CASE(4, 1) SSM_CASE(4, 2) SSM_CASE(4, 4)
-  SSM_CASE(8, 1) SSM_CASE(8, 2)
-#undef SSM_CASE
+static hipError_t dispatch_s(const FwdArgs& a, int S, int64_t nchunks, hipStream_t st) {
+  if (S == 1) return dispatch_flags<IO, 1, MODE>(a, nchunks, st);
+  if (S == 2) return dispatch_flags<IO, 2, MODE>(a, nchunks, st);
+  if (S == 4) return dispatch_flags<IO, 4, MODE>(a, nchunks, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_cs_full(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st) {
-  return bf16 ? dispatch_sg<BF16, kFull>(a, S, G, nchunks, st) : dispatch_sg<F32, kFull>(a, S, G, nchunks, st);
+hipError_t launch_rows_full(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st) {
+  return bf16 ? dispatch_s<BF16, kFull>(a, S, nchunks, st) : dispatch_s<F32, kFull>(a, S, nchunks, st);
 }
 
-hipError_t launch_cs_agg(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st) {
-  return bf16 ? dispatch_sg<BF16, kAgg>(a, S, G, nchunks, st) : dispatch_sg<F32, kAgg>(a, S, G, nchunks, st);
+hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st) {
+  return bf16 ? dispatch_s<BF16, kAgg>(a, S, nchunks, st) : dispatch_s<F32, kAgg>(a, S, nchunks, st);
 }
 
 hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,

@@ -8,7 +8,7 @@ namespace ssm {
 
 enum { kFull = 0, kAgg = 1 };
 
-// Arguments of the channel-serial selective-scan kernel (by value).
+// Arguments of the row-layout selective-scan kernel (by value).
 struct FwdArgs {
   const void* u;
   const void* delta;
@@ -28,17 +28,19 @@ struct FwdArgs {
   int softplus;
 };
 
-// Sizes and flags of one channel-serial launch (by value).
+// Sizes and flags of one row-layout launch (by value).
 struct CsSizes {
   int64_t batch, dim, dstate, L;
   int64_t chunk;
   int softplus;
 };
 
-size_t cs_smem_bytes(int S, int G, int mode);
-int cs_time_tile();
-hipError_t launch_cs_full(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);
-hipError_t launch_cs_agg(const FwdArgs& a, bool bf16, int S, int G, int64_t nchunks, hipStream_t st);
+// S = states per lane (1, 2 or 4); a workgroup is 16 channels x 16 states
+// in 4/S wavefronts.
+size_t rows_smem_bytes(int S, int mode);
+int rows_time_tile();
+hipError_t launch_rows_full(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st);
+hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st);
 hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,
                           hipStream_t st);
 

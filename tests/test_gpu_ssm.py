@@ -87,13 +87,13 @@ def small_inputs(b, d, n, L, dtype=torch.float32, gated=True, with_D=True, with_
 
 # ------------------------------------------------------------ small, complete
 
-@pytest.mark.parametrize("plan,S,chunk", [("auto", 0, 0), ("carry", 2, 0), ("carry", 4, 0), ("carry", 8, 0),
-                                          ("twopass", 2, 64), ("twopass", 4, 128)])
+@pytest.mark.parametrize("plan,S,chunk", [("auto", 0, 0), ("carry", 1, 0), ("carry", 2, 0), ("carry", 4, 0),
+                                          ("twopass", 1, 64), ("twopass", 2, 64), ("twopass", 4, 128)])
 def test_tiny_workload(plan, S, chunk):
     """The tiny workload (b=1, d=64, n=16, L=256, float32, gated, S4D-real A)
     against the NumPy float64 oracle, element by element."""
     inp = workloads.make_inputs(workloads.WORKLOADS["tiny"], device=DEV)
-    y, last = run_gpu(inp, plan=plan, states_per_wave=S, chunk=chunk)
+    y, last = run_gpu(inp, plan=plan, states_per_lane=S, chunk=chunk)
     y_ref, last_ref = ref.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
                                              inp["z"], inp["delta_bias"], True)
     assert rel_err(_host(y), y_ref) <= 1e-4
@@ -128,11 +128,11 @@ def test_optional_inputs(gated, with_D, with_bias, softplus):
     check_all(inp)
 
 
-@pytest.mark.parametrize("S", [2, 4, 8])
+@pytest.mark.parametrize("S", [1, 2, 4])
 @pytest.mark.parametrize("n", [1, 3, 8, 16])
-def test_states_per_wave_and_dstate(S, n):
+def test_states_per_lane_and_dstate(S, n):
     inp = small_inputs(2, 64, n, 160, seed=11 + n)
-    check_all(inp, plan="carry", states_per_wave=S)
+    check_all(inp, plan="carry", states_per_lane=S)
 
 
 @pytest.mark.parametrize("L,chunk", [(256, 64), (1000, 128), (4097, 1024), (5000, 64 * 7)])
@@ -151,7 +151,7 @@ def test_repeat_runs_are_bit_identical():
     """A missing barrier shows up as run-to-run differences; every plan must
     give identical bits on every run."""
     inp = small_inputs(4, 256, 16, 1024, seed=3)
-    for kw in (dict(plan="carry", states_per_wave=2), dict(plan="carry", states_per_wave=8),
+    for kw in (dict(plan="carry", states_per_lane=1), dict(plan="carry", states_per_lane=4),
                dict(plan="twopass", chunk=256)):
         y0, l0 = run_gpu(inp, **kw)
         for _ in range(5):
