@@ -54,6 +54,12 @@ extern "C" {
 #define SSM_PLAN_CARRY   1  /* one launch; each workgroup carries the state
                                over the whole length L */
 #define SSM_PLAN_TWOPASS 2  /* chunk aggregates -> scan over chunks -> fix-up */
+#define SSM_PLAN_MIXED   3  /* carry plan in one launch that mixes blocks of two
+                               16-channel groups at two states per lane with
+                               blocks of one group at one state per lane, so
+                               that every SIMD carries the same number of
+                               (channel, state) chains when the channel groups
+                               number about three per CU */
 
 /*
  * ssm_scan_fwd -- selective-scan forward pass ([Scan page] §1.1-§1.2,
@@ -97,7 +103,8 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
 /*
  * ssm_scan_fwd_plan -- ssm_scan_fwd with an explicit plan
  * ([Scan page] §2.2 and §3.3 describe both decompositions).
- *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY or SSM_PLAN_TWOPASS.
+ *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY, SSM_PLAN_TWOPASS or
+ *                     SSM_PLAN_MIXED (states_per_lane and chunk ignored).
  *   states_per_lane : how many of the d_state states one lane carries for
  *                     its channel (1, 2 or 4; 0 = automatic).  A workgroup
  *                     covers 16 channels and 16 states with 4/states_per_lane
@@ -114,8 +121,9 @@ int ssm_scan_fwd_plan(const void *u, const void *delta, const float *A, const vo
                       int dtype, int plan, int states_per_lane, int64_t chunk, void *stream);
 
 /*
- * ssm_scan_plan_for -- the plan, states per wave and chunk length that
- * SSM_PLAN_AUTO picks for a problem size (host only, no HIP call).
+ * ssm_scan_plan_for -- the plan, states per lane and chunk length that
+ * SSM_PLAN_AUTO picks for a problem size (host only, no HIP call);
+ * states per lane is 0 for SSM_PLAN_MIXED (it uses 2 and 1).
  * Any output pointer may be NULL.  Returns SSM_OK or SSM_EINVAL.
  */
 int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,

@@ -84,6 +84,13 @@ void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, in
   int64_t chunk = L;
   int pl = SSM_PLAN_CARRY;
   int S = states_for(groups);
+  // about three channel groups per CU: one two-group block (S = 2) and one
+  // one-group block (S = 1) per CU give every SIMD three chains per lane,
+  // where S = 2 alone leaves half of the SIMDs with twice the work of the rest
+  if (groups >= 5 * kCUs / 2 && groups < 4 * kCUs && ceil_div(dim, kGroup) >= 3) {
+    pl = SSM_PLAN_MIXED;
+    S = 0;
+  }
   if (groups < kCUs && L >= 2 * kMinChunk) {
     int64_t K = ceil_div(8 * kCUs, groups);
     if (K > L / kMinChunk) K = L / kMinChunk;
@@ -124,7 +131,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (int rc = check_sizes(batch, dim, dstate, L)) return rc;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
   if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
-  if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS)
+  if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS && plan != SSM_PLAN_MIXED)
     return fail(SSM_EINVAL, "unknown plan %d", plan);
   if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4)
     return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", S_req);
@@ -149,6 +156,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   choose(batch, dim, dstate, L, &pl, &S, &chunk);
   if (plan != SSM_PLAN_AUTO) pl = plan;
   if (S_req) S = S_req;
+  if (S == 0) S = 2;  // states per lane of a carry or two-pass plan forced over a mixed choice
   if (pl == SSM_PLAN_TWOPASS) {
     if (chunk_req)
       chunk = chunk_req;
@@ -164,6 +172,13 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SSM_BF16;
 
+  if (pl == SSM_PLAN_MIXED) {
+    a.chunk = L;
+    const int64_t gd = ceil_div(dim, kGroup);
+    hipError_t e = ssm::launch_mixed_full(a, bf16, gd / 3 > 0 ? gd / 3 : 1, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
+    return SSM_OK;
+  }
   if (pl == SSM_PLAN_CARRY) {
     a.chunk = L;
     hipError_t e = ssm::launch_rows_full(a, bf16, S, 1, st);

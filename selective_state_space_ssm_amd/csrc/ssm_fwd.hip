@@ -349,21 +349,49 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // --------------------------------------------------------------------------
-// Row-layout kernel.  Template: storage IO, states per lane S (1, 2, 4),
-// mode, GATED (z present), VEC (L is a multiple of 8: vector loads and
-// stores).  Grid: x = channel group (16 channels), y = batch row,
-// z = chunk.  Block: 64 * (4 / S) threads.  Every pointer is
-// a separate __restrict__ parameter: the caller guarantees that outputs
-// overlap no input.
+// One 16-channel group of the row layout, run by 4/S wavefronts of the
+// block (block-local thread `tid`, wave `wave`), over channels [c0, c0+16)
+// of batch row b and chunk k, with its LDS at `smem`.  Template: storage
+// IO, states per lane S (1, 2, 4), mode, GATED (z present), VEC (L is a
+// multiple of 8: vector loads and stores).  Every wave of the block calls
+// __syncthreads() in the same sequence (all groups of a block have the same
+// tile count).  Pointers: the caller guarantees that outputs overlap no
+// input.
 // --------------------------------------------------------------------------
+template <typename IO>
+struct RowArgs {
+  const typename IO::T* u;
+  const typename IO::T* dlt;
+  const float* Ag;
+  const typename IO::T* Bg;
+  const typename IO::T* Cg;
+  const float* Dg;
+  const typename IO::T* zg;
+  const float* biasg;
+  typename IO::T* yg;
+  float* last_state;
+  const float* h_init;
+  float* agg_p;
+  float* agg_h;
+};
+
 template <typename IO, int S, int MODE, bool GATED, bool VEC>
-__global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(
-    const typename IO::T* __restrict__ u, const typename IO::T* __restrict__ dlt,
-    const float* __restrict__ Ag, const typename IO::T* __restrict__ Bg, const typename IO::T* __restrict__ Cg,
-    const float* __restrict__ Dg, const typename IO::T* __restrict__ zg, const float* __restrict__ biasg,
-    typename IO::T* __restrict__ yg, float* __restrict__ last_state, const float* __restrict__ h_init,
-    float* __restrict__ agg_p, float* __restrict__ agg_h, CsSizes p) {
+__device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSizes& p, float* smem, int tid,
+                                           int wave, int64_t c0, int64_t b, int64_t k) {
   using T = typename IO::T;
+  const T* __restrict__ u = args.u;
+  const T* __restrict__ dlt = args.dlt;
+  const float* __restrict__ Ag = args.Ag;
+  const T* __restrict__ Bg = args.Bg;
+  const T* __restrict__ Cg = args.Cg;
+  const float* __restrict__ Dg = args.Dg;
+  const T* __restrict__ zg = args.zg;
+  const float* __restrict__ biasg = args.biasg;
+  T* __restrict__ yg = args.yg;
+  float* __restrict__ last_state = args.last_state;
+  const float* __restrict__ h_init = args.h_init;
+  float* __restrict__ agg_p = args.agg_p;
+  float* __restrict__ agg_h = args.agg_h;
   constexpr int W = 4 / S;                 // wavefronts
   constexpr int NT = 64 * W;               // threads
   constexpr int NG = 4 * W;                // partial-sum groups (rows of all waves)
@@ -374,22 +402,15 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(
   static_assert(S == 1 || S == 2 || S == 4, "S");
   static_assert(V * NT == kCG * kTT && BCQ * NT * 4 == 2 * kNS * kTT, "tiling");
 
-  extern __shared__ float smem[];
   float* sDt = smem;                  // [16][kRow]  Delta2
   float* sDu = sDt + kCG * kRow;      // [16][kRow]  Delta * u
   float* sBC = sDu + kCG * kRow;      // [2][16][kTT] B rows, then C rows (float32)
   float* sP = sBC + 2 * kNS * kTT;    // [NG][16][kRow] partial y (kFull only)
 
-  const int tid = threadIdx.x;
-  // the wave index as an SGPR keeps every per-wave quantity uniform
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int row = lane >> 4;
   const int col = lane & 15;
   const int64_t dim = p.dim, L = p.L, N = p.dstate;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kCG;
-  const int64_t b = blockIdx.y;
-  const int64_t k = blockIdx.z;
   // time indices fit in 32 bits (the host rejects L >= 2^31)
   const int Li = static_cast<int>(L);
   const int t_begin = static_cast<int>(k * p.chunk);
@@ -426,8 +447,9 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(
   // past d_inner and states past d_state lie past the resource's size: they
   // read as zero and their writes are dropped.  Byte offsets fit in 32 bits
   // (the host bounds 16 * L * element size).
-  const int64_t rows_here = (dim - c0 < kCG) ? dim - c0 : kCG;
-  const int64_t row0 = (b * dim + c0) * L;
+  const int64_t rows_left = dim - c0;  // may be <= 0 for a padding group of a mixed block
+  const int64_t rows_here = rows_left < 0 ? 0 : (rows_left < kCG ? rows_left : kCG);
+  const int64_t row0 = (b * dim + (rows_here > 0 ? c0 : 0)) * L;
   const uint32_t in_bytes = static_cast<uint32_t>(rows_here * L * ES);
   const Rsrc rU = make_rsrc(u + row0, in_bytes);
   const Rsrc rD = make_rsrc(dlt + row0, in_bytes);
@@ -742,6 +764,56 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(
 }
 
 // --------------------------------------------------------------------------
+// Kernels.
+//  ssm_rows_kernel: one 16-channel group per block.  Grid: x = channel
+//    group, y = batch row, z = chunk; block 64 * (4 / S) threads.
+//  ssm_mixed_kernel: blocks of 256 threads of two kinds, so that a CU that
+//    holds one of each gives every SIMD three (channel, state) chains per
+//    lane: blocks [0, nA) run two groups at two states per lane (waves 0-1
+//    and 2-3), blocks [nA, nA + nB) one group at one state per lane.  Grid:
+//    x = nA + nB (all two-group blocks first, so that consecutive launches
+//    of each kind spread over the CUs), z = chunk.  Per batch row,
+//    groups [0, 2*pairs) belong to two-group blocks and the rest to
+//    one-group blocks.
+// --------------------------------------------------------------------------
+template <typename IO, int S, int MODE, bool GATED, bool VEC>
+__global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(RowArgs<IO> args, CsSizes p) {
+  extern __shared__ float smem[];
+  const int tid = threadIdx.x;
+  // the wave index as an SGPR keeps every per-wave quantity uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  rows_group<IO, S, MODE, GATED, VEC>(args, p, smem, tid, wave, static_cast<int64_t>(blockIdx.x) * kCG,
+                                      blockIdx.y, blockIdx.z);
+}
+
+struct MixedSizes {
+  int64_t pairs;    // two-group blocks per batch row
+  int64_t singles;  // one-group blocks per batch row
+};
+
+template <typename IO, int MODE, bool GATED, bool VEC>
+__global__ __launch_bounds__(256, 2) void ssm_mixed_kernel(RowArgs<IO> args, CsSizes p, MixedSizes m,
+                                                           int smem_pair_floats) {
+  extern __shared__ float smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nA = p.batch * m.pairs;
+  const int64_t x = blockIdx.x;
+  if (x < nA) {
+    const int sub = wave >> 1;
+    const int64_t b = x / m.pairs;
+    const int64_t g = 2 * (x % m.pairs) + sub;
+    rows_group<IO, 2, MODE, GATED, VEC>(args, p, smem + sub * smem_pair_floats, tid - 128 * sub, wave & 1,
+                                        g * kCG, b, blockIdx.z);
+  } else {
+    const int64_t q = x - nA;
+    const int64_t b = q / m.singles;
+    const int64_t g = 2 * m.pairs + q % m.singles;
+    rows_group<IO, 1, MODE, GATED, VEC>(args, p, smem, tid, wave, g * kCG, b, blockIdx.z);
+  }
+}
+
+// --------------------------------------------------------------------------
 // Chunk combine: for every (b, n, d), run the carry over the K chunk totals,
 //   h_init^(0) = 0,  h_init^(k) = P^(k-1) h_init^(k-1) + H^(k-1)
 // ([Scan page] §3.3 fix-up), writing h_init for k = 0..K-1.  One thread per
@@ -771,9 +843,25 @@ size_t rows_smem_bytes(int S, int mode) {
 
 int rows_time_tile() { return kTT; }
 
+template <typename IO>
+static RowArgs<IO> row_args(const FwdArgs& a) {
+  using T = typename IO::T;
+  RowArgs<IO> r;
+  r.u = static_cast<const T*>(a.u); r.dlt = static_cast<const T*>(a.delta); r.Ag = a.A;
+  r.Bg = static_cast<const T*>(a.B); r.Cg = static_cast<const T*>(a.C); r.Dg = a.D;
+  r.zg = static_cast<const T*>(a.z); r.biasg = a.bias; r.yg = static_cast<T*>(a.y);
+  r.last_state = a.last_state; r.h_init = a.h_init; r.agg_p = a.agg_p; r.agg_h = a.agg_h;
+  return r;
+}
+
+static CsSizes cs_sizes(const FwdArgs& a) {
+  CsSizes sz;
+  sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.chunk = a.chunk; sz.softplus = a.softplus;
+  return sz;
+}
+
 template <typename IO, int S, int MODE, bool GATED, bool VEC>
 static hipError_t launch_rows_v(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
-  using T = typename IO::T;
   const dim3 grid(static_cast<unsigned>((a.dim + kCG - 1) / kCG), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(nchunks));
   const size_t smem = rows_smem_bytes(S, MODE);
@@ -781,13 +869,38 @@ static hipError_t launch_rows_v(const FwdArgs& a, int64_t nchunks, hipStream_t s
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  CsSizes sz;
-  sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.chunk = a.chunk; sz.softplus = a.softplus;
-  hipLaunchKernelGGL(kern, grid, dim3(256 / S), smem, st, static_cast<const T*>(a.u),
-                     static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
-                     a.D, static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.last_state, a.h_init,
-                     a.agg_p, a.agg_h, sz);
+  hipLaunchKernelGGL(kern, grid, dim3(256 / S), smem, st, row_args<IO>(a), cs_sizes(a));
   return hipGetLastError();
+}
+
+template <typename IO, int MODE, bool GATED, bool VEC>
+static hipError_t launch_mixed_v(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
+  const int64_t groups = (a.dim + kCG - 1) / kCG;
+  MixedSizes m;
+  m.pairs = pairs;
+  m.singles = groups - 2 * pairs;
+  const size_t pair_bytes = rows_smem_bytes(2, MODE);
+  const size_t smem = (2 * pair_bytes > rows_smem_bytes(1, MODE)) ? 2 * pair_bytes : rows_smem_bytes(1, MODE);
+  const dim3 grid(static_cast<unsigned>(a.batch * (m.pairs + m.singles)), 1, static_cast<unsigned>(nchunks));
+  auto kern = ssm_mixed_kernel<IO, MODE, GATED, VEC>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, row_args<IO>(a), cs_sizes(a), m,
+                     static_cast<int>(pair_bytes / sizeof(float)));
+  return hipGetLastError();
+}
+
+template <typename IO, int MODE>
+static hipError_t dispatch_mixed(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
+  const bool vec = a.L % 8 == 0;
+  if constexpr (MODE == kFull) {
+    if (a.z != nullptr)
+      return vec ? launch_mixed_v<IO, MODE, true, true>(a, pairs, nchunks, st)
+                 : launch_mixed_v<IO, MODE, true, false>(a, pairs, nchunks, st);
+  }
+  return vec ? launch_mixed_v<IO, MODE, false, true>(a, pairs, nchunks, st)
+             : launch_mixed_v<IO, MODE, false, false>(a, pairs, nchunks, st);
 }
 
 template <typename IO, int S, int MODE>
@@ -816,6 +929,10 @@ hipError_t launch_rows_full(const FwdArgs& a, bool bf16, int S, int64_t nchunks,
 
 hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st) {
   return bf16 ? dispatch_s<BF16, kAgg>(a, S, nchunks, st) : dispatch_s<F32, kAgg>(a, S, nchunks, st);
+}
+
+hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t nchunks, hipStream_t st) {
+  return bf16 ? dispatch_mixed<BF16, kFull>(a, pairs, nchunks, st) : dispatch_mixed<F32, kFull>(a, pairs, nchunks, st);
 }
 
 hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,

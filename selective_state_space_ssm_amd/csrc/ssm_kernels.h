@@ -41,6 +41,9 @@ size_t rows_smem_bytes(int S, int mode);
 int rows_time_tile();
 hipError_t launch_rows_full(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st);
 hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, hipStream_t st);
+// Mixed launch: per batch row, `pairs` blocks of two groups at S = 2 and the
+// remaining groups at S = 1 (one group per block).
+hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t nchunks, hipStream_t st);
 hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,
                           hipStream_t st);
 

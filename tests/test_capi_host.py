@@ -103,7 +103,11 @@ def test_affine_scan_rejects_bad_arguments():
 def test_plan_choice():
     # many channels: carry plan over the whole length
     p = ssm.plan_for(8, 1536, 16, 2048)
-    assert p["plan"] == "carry" and p["chunk"] == 2048
+    assert p["plan"] == "mixed" and p["chunk"] == 2048  # 768 groups: three per CU
+    p = ssm.plan_for(8, 4096, 16, 2048, "bf16")
+    assert p["plan"] == "carry" and p["states_per_lane"] == 4
+    p = ssm.plan_for(4, 1536, 16, 2048)
+    assert p["plan"] == "carry" and p["states_per_lane"] == 2
     p = ssm.plan_for(16, 5120, 16, 8192, "bf16")
     assert p["plan"] == "carry"
     # few channels, very long sequence: two-pass over chunks that are multiples of 64

@@ -88,7 +88,8 @@ def small_inputs(b, d, n, L, dtype=torch.float32, gated=True, with_D=True, with_
 # ------------------------------------------------------------ small, complete
 
 @pytest.mark.parametrize("plan,S,chunk", [("auto", 0, 0), ("carry", 1, 0), ("carry", 2, 0), ("carry", 4, 0),
-                                          ("twopass", 1, 64), ("twopass", 2, 64), ("twopass", 4, 128)])
+                                          ("mixed", 0, 0), ("twopass", 1, 64), ("twopass", 2, 64),
+                                          ("twopass", 4, 128)])
 def test_tiny_workload(plan, S, chunk):
     """The tiny workload (b=1, d=64, n=16, L=256, float32, gated, S4D-real A)
     against the NumPy float64 oracle, element by element."""
@@ -121,6 +122,17 @@ def test_ragged_shapes(shape, dtype):
     check_all(inp)
 
 
+@pytest.mark.parametrize("shape", [(1, 64, 16, 100), (2, 130, 16, 257), (3, 200, 5, 1000), (1, 48, 16, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_mixed_plan(shape, dtype):
+    """Blocks of two 16-channel groups at two states per lane next to blocks
+    of one group at one state per lane (ragged channel and step tails
+    included) give the oracle's result."""
+    inp = small_inputs(*shape, dtype=dtype, seed=3 + sum(shape))
+    check_all(inp, plan="mixed")
+
+
 @pytest.mark.parametrize("gated,with_D,with_bias,softplus", [
     (False, False, False, True), (True, False, True, False), (False, True, False, False), (True, True, True, True)])
 def test_optional_inputs(gated, with_D, with_bias, softplus):
@@ -151,7 +163,7 @@ def test_repeat_runs_are_bit_identical():
     """A missing barrier shows up as run-to-run differences; every plan must
     give identical bits on every run."""
     inp = small_inputs(4, 256, 16, 1024, seed=3)
-    for kw in (dict(plan="carry", states_per_lane=1), dict(plan="carry", states_per_lane=4),
+    for kw in (dict(plan="carry", states_per_lane=1), dict(plan="carry", states_per_lane=4), dict(plan="mixed"),
                dict(plan="twopass", chunk=256)):
         y0, l0 = run_gpu(inp, **kw)
         for _ in range(5):
