@@ -53,6 +53,10 @@ def parse():
     p.add_argument("--chunk", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="budget for the CPU oracle baseline (0 disables it)")
+    p.add_argument("--h0", action="store_true",
+                   help="start every channel from a random state (ssm_scan_fwd_states)")
+    p.add_argument("--state-chunk", type=int, default=0,
+                   help="also write the state every STATE_CHUNK steps (ssm_scan_fwd_states)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -178,9 +182,25 @@ def main():
     last = torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32)
     kw = dict(plan=args.plan, states_per_lane=args.states_per_lane, chunk=args.chunk, y=y, last_state=last)
 
-    def step():
-        ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                         inp["delta_bias"], delta_softplus=w.softplus, **kw)
+    use_states = args.h0 or args.state_chunk > 0
+    extra_bytes = 0
+    if use_states:
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        h0 = torch.randn((w.batch, w.dim, w.dstate), generator=g, device=dev) if args.h0 else None
+        K = -(-w.L // args.state_chunk) if args.state_chunk > 0 else 0
+        cs = torch.empty((w.batch, K, w.dim, w.dstate), device=dev) if K else None
+        extra_bytes = 4 * w.batch * w.dim * w.dstate * (int(args.h0) + K)
+
+        def step():
+            ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                    inp["delta_bias"], delta_softplus=w.softplus, h0=h0,
+                                    state_chunk=args.state_chunk, plan=args.plan, y=y, last_state=last,
+                                    chunk_states=cs)
+    else:
+        def step():
+            ssm.ssm_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                             inp["delta_bias"], delta_softplus=w.softplus, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -203,13 +223,13 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     ms_wall = wall * 1e3 / args.steps
 
-    bytes_alg = w.algorithmic_bytes()
+    bytes_alg = w.algorithmic_bytes() + extra_bytes
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     plan = ssm.plan_for(w.batch, w.dim, w.dstate, w.L, w.dtype)
     if args.plan != "auto":
         plan["plan"] = args.plan
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name, plan)
+    traffic = None if use_states else measured_traffic(w.name, plan)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -225,7 +245,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and value recipes of the workload)",
         "config": {"workload": w.name, "batch": w.batch, "d_inner": w.dim, "d_state": w.dstate, "seq_len": w.L,
-                   "io_dtype": w.dtype, "gated": w.gated, "plan": plan},
+                   "io_dtype": w.dtype, "gated": w.gated, "plan": plan,
+                   **({"h0": True} if args.h0 else {}),
+                   **({"state_chunk": args.state_chunk} if args.state_chunk else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),

@@ -121,6 +121,30 @@ int ssm_scan_fwd_plan(const void *u, const void *delta, const float *A, const vo
                       int dtype, int plan, int states_per_lane, int64_t chunk, void *stream);
 
 /*
+ * ssm_scan_fwd_states -- ssm_scan_fwd from a given start state, keeping the
+ * state at every chunk boundary.  Starting from any h_0 is the
+ * h_t = A_t h_0 + B_t form of [Scan page] §2.1; the boundary states are the
+ * checkpoints that the chunked recomputation of [Mamba-2 page] §4.3 keeps
+ * (h_0, h_c, h_2c, ...), from which any chunk can be recomputed alone.
+ *   h0           : [batch, d_inner, d_state] float32 start state, nullable
+ *                  (zero).  An input: must not overlap any output.
+ *   chunk_states : [batch, K, d_inner, d_state] float32 output, nullable,
+ *                  K = ceil(L / state_chunk).  Entry k is the state after
+ *                  step min((k+1)*state_chunk, L) - 1, so entry K-1 equals
+ *                  last_state.
+ *   state_chunk  : steps between saved states, a positive multiple of 32
+ *                  when chunk_states is given (ignored otherwise).
+ *   plan         : as for ssm_scan_fwd_plan (states per lane and chunk are
+ *                  chosen automatically).
+ * Other arguments, semantics and errors as ssm_scan_fwd.
+ */
+int ssm_scan_fwd_states(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                        const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                        const float *h0, void *y, float *last_state, float *chunk_states, int64_t state_chunk,
+                        int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int plan,
+                        void *stream);
+
+/*
  * ssm_scan_plan_for -- the plan, states per lane and chunk length that
  * SSM_PLAN_AUTO picks for a problem size (host only, no HIP call);
  * states per lane is 0 for SSM_PLAN_MIXED (it uses 2 and 1).

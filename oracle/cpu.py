@@ -27,6 +27,9 @@ def lib():
         L.ssm_oracle_fwd_rows.argtypes = [P, P, P, P, P, I64, P, P, P, P, P, ctypes.c_int,
                                           I64, I64, I64, I64, P, P, ctypes.c_int]
         L.ssm_oracle_fwd_rows.restype = ctypes.c_int
+        L.ssm_oracle_fwd_rows_h0.argtypes = [P, P, P, P, P, I64, P, P, P, P, P, ctypes.c_int,
+                                             I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
+        L.ssm_oracle_fwd_rows_h0.restype = ctypes.c_int
         L.affine_scan_serial_f32.argtypes = [P, P, P, P, I64, I64]
         L.affine_scan_serial_f32.restype = None
         L.affine_scan_replay_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -49,13 +52,15 @@ def _f32(x):
 
 
 def fwd_rows(u_rows, delta_rows, z_rows, row_b, row_d, A, B, C, D, delta_bias,
-             delta_softplus, batch, dim, dstate, L, want_y=True, nthreads=0):
+             delta_softplus, batch, dim, dstate, L, want_y=True, nthreads=0, h0_rows=None, chunk=0):
     """float64 selective-scan forward for selected (batch, channel) rows.
 
     u_rows, delta_rows, z_rows: [nrows, L] (float32-representable values);
     row_b, row_d: [nrows] indices; A [dim, dstate]; B, C [batch, dstate, L];
-    D, delta_bias [dim] or None.  Returns (y [nrows, L] or None,
-    last_state [nrows, dstate]).
+    D, delta_bias [dim] or None; h0_rows: [nrows, dstate] start states or
+    None (zero).  Returns (y [nrows, L] or None, last_state [nrows, dstate]),
+    and with chunk > 0 also the chunk-boundary states
+    [nrows, ceil(L/chunk), dstate] (state after step min((k+1)*chunk, L)-1).
     """
     u_rows = _f32(u_rows); delta_rows = _f32(delta_rows); z_rows = _f32(z_rows)
     A = _f32(A); B = _f32(B); C = _f32(C); D = _f32(D); delta_bias = _f32(delta_bias)
@@ -64,12 +69,18 @@ def fwd_rows(u_rows, delta_rows, z_rows, row_b, row_d, A, B, C, D, delta_bias,
     nrows = row_b.shape[0]
     y = np.empty((nrows, L), dtype=np.float64) if want_y else None
     last = np.empty((nrows, dstate), dtype=np.float64)
-    rc = lib().ssm_oracle_fwd_rows(_ptr(u_rows), _ptr(delta_rows), _ptr(z_rows), _ptr(row_b), _ptr(row_d),
-                                   nrows, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias),
-                                   int(bool(delta_softplus)), batch, dim, dstate, L, _ptr(y), _ptr(last),
-                                   int(nthreads))
+    h0 = None if h0_rows is None else np.ascontiguousarray(
+        h0_rows.detach().cpu().double().numpy() if hasattr(h0_rows, "detach") else h0_rows, dtype=np.float64)
+    K = (L + chunk - 1) // chunk if chunk else 0
+    bounds = np.empty((nrows, K, dstate), dtype=np.float64) if chunk else None
+    rc = lib().ssm_oracle_fwd_rows_h0(_ptr(u_rows), _ptr(delta_rows), _ptr(z_rows), _ptr(row_b), _ptr(row_d),
+                                      nrows, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias),
+                                      int(bool(delta_softplus)), batch, dim, dstate, L, _ptr(h0), int(chunk),
+                                      _ptr(bounds), _ptr(y), _ptr(last), int(nthreads))
     if rc != 0:
-        raise ValueError("ssm_oracle_fwd_rows rejected its arguments")
+        raise ValueError("ssm_oracle_fwd_rows_h0 rejected its arguments")
+    if chunk:
+        return y, last, bounds
     return y, last
 
 

@@ -47,14 +47,43 @@ static double silu_d(double z) {
  * nthreads threads (nthreads <= 0: runtime default).  Returns 0, or 1 on a
  * bad argument.
  */
+int ssm_oracle_fwd_rows_h0(const float *u_rows, const float *delta_rows, const float *z_rows,
+                           const int64_t *row_b, const int64_t *row_d, int64_t nrows,
+                           const float *A, const float *B, const float *C, const float *D,
+                           const float *delta_bias, int delta_softplus,
+                           int64_t batch, int64_t dim, int64_t dstate, int64_t L,
+                           const double *h0_rows, int64_t chunk, double *bounds,
+                           double *y, double *last_state, int nthreads);
+
 int ssm_oracle_fwd_rows(const float *u_rows, const float *delta_rows, const float *z_rows,
                         const int64_t *row_b, const int64_t *row_d, int64_t nrows,
                         const float *A, const float *B, const float *C, const float *D,
                         const float *delta_bias, int delta_softplus,
                         int64_t batch, int64_t dim, int64_t dstate, int64_t L,
                         double *y, double *last_state, int nthreads) {
+    return ssm_oracle_fwd_rows_h0(u_rows, delta_rows, z_rows, row_b, row_d, nrows, A, B, C, D, delta_bias,
+                                  delta_softplus, batch, dim, dstate, L, NULL, 0, NULL, y, last_state, nthreads);
+}
+
+/*
+ * The same recurrence started from a given state and keeping the state at
+ * every chunk boundary ([Scan page] §2.1: h_t = A_t h_0 + B_t for any start
+ * state; [Mamba-2 page] §4.3: the chunked recomputation keeps h at every
+ * chunk boundary).  h0_rows: [nrows, dstate] or NULL (zero).  With chunk > 0
+ * and bounds non-NULL, bounds[r, k, n] (k = 0 .. ceil(L/chunk) - 1) is the
+ * state after step min((k+1)*chunk, L) - 1.
+ */
+int ssm_oracle_fwd_rows_h0(const float *u_rows, const float *delta_rows, const float *z_rows,
+                           const int64_t *row_b, const int64_t *row_d, int64_t nrows,
+                           const float *A, const float *B, const float *C, const float *D,
+                           const float *delta_bias, int delta_softplus,
+                           int64_t batch, int64_t dim, int64_t dstate, int64_t L,
+                           const double *h0_rows, int64_t chunk, double *bounds,
+                           double *y, double *last_state, int nthreads) {
     if (!u_rows || !delta_rows || !row_b || !row_d || !A || !B || !C) return 1;
-    if (nrows < 0 || batch <= 0 || dim <= 0 || dstate <= 0 || L < 0) return 1;
+    if (nrows < 0 || batch <= 0 || dim <= 0 || dstate <= 0 || L < 0 || chunk < 0) return 1;
+    if (bounds && chunk == 0) return 1;
+    const int64_t K = chunk > 0 ? (L + chunk - 1) / chunk : 0;
     for (int64_t r = 0; r < nrows; ++r)
         if (row_b[r] < 0 || row_b[r] >= batch || row_d[r] < 0 || row_d[r] >= dim) return 1;
 #ifdef _OPENMP
@@ -68,6 +97,8 @@ int ssm_oracle_fwd_rows(const float *u_rows, const float *delta_rows, const floa
         const int64_t b = row_b[r], d = row_d[r];
         double *h = (double *)calloc((size_t)dstate, sizeof(double));
         if (!h) { bad = 1; continue; }
+        if (h0_rows)
+            for (int64_t n = 0; n < dstate; ++n) h[n] = h0_rows[r * dstate + n];
         const float *ur = u_rows + r * L;
         const float *dr = delta_rows + r * L;
         const float *zr = z_rows ? z_rows + r * L : NULL;
@@ -87,6 +118,8 @@ int ssm_oracle_fwd_rows(const float *u_rows, const float *delta_rows, const floa
             acc += Dd * uu;
             if (zr) acc *= silu_d((double)zr[t]);
             if (y) y[r * L + t] = acc;
+            if (bounds && ((t + 1) % chunk == 0 || t + 1 == L))
+                for (int64_t n = 0; n < dstate; ++n) bounds[(r * K + t / chunk) * dstate + n] = h[n];
         }
         if (last_state)
             for (int64_t n = 0; n < dstate; ++n) last_state[r * dstate + n] = h[n];

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +57,8 @@ def load_library():
     lib.ssm_scan_fwd.restype = I
     lib.ssm_scan_fwd_plan.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, I, I, I64, P]
     lib.ssm_scan_fwd_plan.restype = I
+    lib.ssm_scan_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.ssm_scan_fwd_states.restype = I
     lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
                                       ctypes.POINTER(I64)]
     lib.ssm_scan_plan_for.restype = I
@@ -148,6 +150,71 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                                    PLANS[plan], int(states_per_lane), int(chunk), _stream(device))
     _check(rc)
     return y, last_state
+
+
+def ssm_scan_fwd_states(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                        C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                        delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                        h0: Optional[torch.Tensor] = None, state_chunk: int = 0, plan: str = "auto",
+                        y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+                        chunk_states: Optional[torch.Tensor] = None):
+    """Selective-scan forward from a start state h0 [b, d, n] (float32, or
+    None for zero), also returning the states at every ``state_chunk`` steps
+    (see ``ssm_scan_fwd_states`` in include/ssm_scan.h).
+
+    Returns (y, last_state, chunk_states [b, ceil(L/state_chunk), d, n] or
+    None when state_chunk is 0).
+    """
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_fwd_states needs CUDA/HIP tensors")
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [b, d, L] and A [d, n]")
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    dt = u.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    for t, name, shape in ((u, "u", (bsz, dim, L)), (delta, "delta", (bsz, dim, L)), (B, "B", (bsz, n, L)),
+                           (C, "C", (bsz, n, L))):
+        _need(t, name, dt, device, shape)
+    _need(A, "A", torch.float32, device, (dim, n))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    if D is not None:
+        _need(D, "D", torch.float32, device, (dim,))
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", torch.float32, device, (dim,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, device, (bsz, dim, n))
+    if plan not in PLANS:
+        raise ValueError(f"plan must be one of {list(PLANS)}")
+    if state_chunk < 0:
+        raise ValueError("state_chunk must be >= 0")
+    if y is None:
+        y = torch.empty_like(u)
+    else:
+        _need(y, "y", dt, device, (bsz, dim, L))
+    if last_state is None:
+        last_state = torch.empty((bsz, dim, n), device=device, dtype=torch.float32)
+    else:
+        _need(last_state, "last_state", torch.float32, device, (bsz, dim, n))
+    if state_chunk > 0:
+        K = -(-L // state_chunk)
+        if chunk_states is None:
+            chunk_states = torch.empty((bsz, K, dim, n), device=device, dtype=torch.float32)
+        else:
+            _need(chunk_states, "chunk_states", torch.float32, device, (bsz, K, dim, n))
+    else:
+        chunk_states = None
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_fwd_states(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(y),
+                                     _ptr(last_state), _ptr(chunk_states), int(state_chunk), bsz, dim, n, L,
+                                     SSM_F32 if dt == torch.float32 else SSM_BF16, PLANS[plan], _stream(device))
+    _check(rc)
+    return y, last_state, chunk_states
 
 
 def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,

@@ -122,9 +122,9 @@ int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t L) {
 }
 
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                  const void* z, const float* delta_bias, int delta_softplus, void* y, float* last_state,
-                  int64_t batch, int64_t dim, int64_t dstate, int64_t L, int dtype, int plan, int S_req,
-                  int64_t chunk_req, void* stream) {
+                  const void* z, const float* delta_bias, int delta_softplus, const float* h0, void* y,
+                  float* last_state, float* chunk_states, int64_t state_chunk, int64_t batch, int64_t dim,
+                  int64_t dstate, int64_t L, int dtype, int plan, int S_req, int64_t chunk_req, void* stream) {
   g_err.clear();
   if (!u || !delta || !A || !B || !C || !y)
     return fail(SSM_EINVAL, "u, delta, A, B, C and y must not be NULL");
@@ -136,20 +136,27 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4)
     return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", S_req);
   if (chunk_req < 0 || chunk_req % 64 != 0) return fail(SSM_EINVAL, "chunk must be 0 or a positive multiple of 64");
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, last_state};
+  if (chunk_states != nullptr && (state_chunk <= 0 || state_chunk % ssm::rows_time_tile() != 0))
+    return fail(SSM_EINVAL, "state_chunk must be a positive multiple of %d when chunk_states is given",
+                ssm::rows_time_tile());
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, chunk_states};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
 
   const uint64_t es = dtype == SSM_F32 ? 4 : 2;
   const uint64_t nbdl = uint64_t(batch) * dim * L, nbnl = uint64_t(batch) * dstate * L;
+  const uint64_t nstate = uint64_t(batch) * dim * dstate;
+  const uint64_t nsc = chunk_states ? uint64_t((L + state_chunk - 1) / state_chunk) : 0;
   const Range rin[] = {range_of(u, nbdl * es), range_of(delta, nbdl * es), range_of(z, nbdl * es),
                        range_of(B, nbnl * es), range_of(C, nbnl * es), range_of(A, uint64_t(dim) * dstate * 4),
-                       range_of(D, uint64_t(dim) * 4), range_of(delta_bias, uint64_t(dim) * 4)};
+                       range_of(D, uint64_t(dim) * 4), range_of(delta_bias, uint64_t(dim) * 4),
+                       range_of(h0, nstate * 4)};
   const Range ry = range_of(y, nbdl * es);
-  const Range rl = range_of(last_state, uint64_t(batch) * dim * dstate * 4);
+  const Range rl = range_of(last_state, nstate * 4);
+  const Range rc = range_of(chunk_states, nsc * nstate * 4);
   for (const Range& r : rin)
-    if (overlap(ry, r) || overlap(rl, r)) return fail(SSM_EINVAL, "outputs must not overlap inputs");
-  if (overlap(ry, rl)) return fail(SSM_EINVAL, "y and last_state overlap");
+    if (overlap(ry, r) || overlap(rl, r) || overlap(rc, r)) return fail(SSM_EINVAL, "outputs must not overlap inputs");
+  if (overlap(ry, rl) || overlap(ry, rc) || overlap(rl, rc)) return fail(SSM_EINVAL, "outputs overlap each other");
 
   int pl, S;
   int64_t chunk;
@@ -168,6 +175,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   ssm::FwdArgs a{};
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
   a.y = y; a.last_state = last_state; a.h_init = nullptr; a.agg_p = nullptr; a.agg_h = nullptr;
+  a.h0 = h0; a.chunk_states = chunk_states; a.state_chunk = chunk_states ? state_chunk : 0;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.L = L; a.softplus = delta_softplus;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SSM_BF16;
@@ -202,7 +210,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   a.agg_p = agg_p;
   a.agg_h = agg_h;
   e = ssm::launch_rows_agg(a, bf16, S, K - 1, st);
-  if (e == hipSuccess) e = ssm::launch_combine(agg_p, agg_h, h_init, rows, K, st);
+  if (e == hipSuccess) e = ssm::launch_combine(agg_p, agg_h, h0, h_init, batch, dim, dstate, K, st);
   if (e == hipSuccess) {
     a.agg_p = nullptr;
     a.agg_h = nullptr;
@@ -222,16 +230,24 @@ extern "C" {
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* delta_bias, int delta_softplus, void* y, float* last_state,
                  int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, void* stream) {
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, last_state, batch, d_inner, d_state,
-                       L, dtype, SSM_PLAN_AUTO, 0, 0, stream);
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
+                       d_inner, d_state, L, dtype, SSM_PLAN_AUTO, 0, 0, stream);
 }
 
 int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const void* B, const void* C,
                       const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
                       float* last_state, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
                       int plan, int states_per_lane, int64_t chunk, void* stream) {
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, last_state, batch, d_inner, d_state,
-                       L, dtype, plan, states_per_lane, chunk, stream);
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
+                       d_inner, d_state, L, dtype, plan, states_per_lane, chunk, stream);
+}
+
+int ssm_scan_fwd_states(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                        void* y, float* last_state, float* chunk_states, int64_t state_chunk, int64_t batch,
+                        int64_t d_inner, int64_t d_state, int64_t L, int dtype, int plan, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, y, last_state, chunk_states,
+                       state_chunk, batch, d_inner, d_state, L, dtype, plan, 0, 0, stream);
 }
 
 int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int* plan,

@@ -45,8 +45,11 @@
 // no masking and only the stores are guarded.
 //
 // Modes (template MODE):
-//   kFull: start from zero or from a per-chunk start state, emit y over
-//          [chunk*k, chunk*(k+1)), and last_state from the chunk that ends at L.
+//   kFull: start from zero, from the caller's h0 or from a per-chunk start
+//          state, emit y over [chunk*k, chunk*(k+1)), last_state from the
+//          chunk that ends at L, and optionally the state after every tile
+//          that ends a state chunk (the checkpoints of the Mamba-2 page's
+//          §4.3 chunked recomputation).
 //   kAgg:  start from zero, emit only the chunk aggregate
 //          (P_n = exp2(A_n * sum Delta2), H_n = h_n at the chunk end),
 //          i.e. the chunk total (A^(k), B^(k)) of [Scan page] §2.2 / §3.3.
@@ -371,6 +374,8 @@ struct RowArgs {
   typename IO::T* yg;
   float* last_state;
   const float* h_init;
+  const float* h0;
+  float* chunk_states;
   float* agg_p;
   float* agg_h;
 };
@@ -390,6 +395,8 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   T* __restrict__ yg = args.yg;
   float* __restrict__ last_state = args.last_state;
   const float* __restrict__ h_init = args.h_init;
+  const float* __restrict__ h0 = args.h0;
+  float* __restrict__ chunk_states = args.chunk_states;
   float* __restrict__ agg_p = args.agg_p;
   float* __restrict__ agg_h = args.agg_h;
   constexpr int W = 4 / S;                 // wavefronts
@@ -428,7 +435,15 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     const bool ok = dvalid && n < N;
     An[s] = ok ? Ag[d * N + n] : 0.0f;
     h[s] = 0.0f;
-    if (MODE == kFull && h_init != nullptr && ok) h[s] = h_init[((k * p.batch + b) * N + n) * dim + d];
+    // start state: the chunk start state of the two-pass plan (which already
+    // includes h0), else h0 for the single-chunk plans; the aggregate pass
+    // always starts from zero
+    if (MODE == kFull && ok) {
+      if (h_init != nullptr)
+        h[s] = h_init[((k * p.batch + b) * N + n) * dim + d];
+      else if (h0 != nullptr)
+        h[s] = h0[(b * dim + d) * N + n];
+    }
   }
   float dsum = 0.0f;  // kAgg: sum of Delta2 over the chunk
 
@@ -727,8 +742,28 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   }
   load_tile(A, t_begin + 2 * kTT);
   __syncthreads();
+  // State after the tile [t0, t0 + kTT) when it ends a state chunk (or the
+  // sequence): the checkpoint of the Mamba-2 page §4.3 chunked recompute.
+  const int sc = static_cast<int>(p.state_chunk);
+  const int64_t nsc = sc > 0 ? (L + sc - 1) / sc : 0;
+  auto save_states = [&](int t0) {
+    if (MODE != kFull || chunk_states == nullptr || t0 >= t_end) return;
+    const int te = t0 + kTT;
+    int64_t kc = -1;
+    if (te <= Li && te % sc == 0)
+      kc = te / sc - 1;
+    else if (te >= Li && t_end == Li)
+      kc = nsc - 1;
+    if (kc < 0 || !dvalid) return;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t n = static_cast<int64_t>(grp) * S + s;
+      if (n < N) chunk_states[((b * nsc + kc) * dim + d) * N + n] = h[s];
+    }
+  };
   auto half_step = [&](int t0, TileRegs& next, TileRegs& reload) {
     recur();
+    save_states(t0);
     __syncthreads();
     prep(next);
     if (MODE == kFull) epilogue(t0);
@@ -815,17 +850,23 @@ __global__ __launch_bounds__(256, 2) void ssm_mixed_kernel(RowArgs<IO> args, CsS
 
 // --------------------------------------------------------------------------
 // Chunk combine: for every (b, n, d), run the carry over the K chunk totals,
-//   h_init^(0) = 0,  h_init^(k) = P^(k-1) h_init^(k-1) + H^(k-1)
+//   h_init^(0) = h0 (zero if absent),  h_init^(k) = P^(k-1) h_init^(k-1) + H^(k-1)
 // ([Scan page] §3.3 fix-up), writing h_init for k = 0..K-1.  One thread per
 // (b, n, d); d is contiguous, so every access is coalesced.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void ssm_combine_kernel(const float* __restrict__ agg_p,
                                                           const float* __restrict__ agg_h,
-                                                          float* __restrict__ h_init, int64_t rows,
-                                                          int64_t K) {
+                                                          const float* __restrict__ h0,
+                                                          float* __restrict__ h_init, int64_t batch, int64_t dim,
+                                                          int64_t dstate, int64_t K) {
+  const int64_t rows = batch * dstate * dim;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= rows) return;
-  float hv = 0.0f;
+  // row i = (b, n, d) with d fastest; h0 is [b][d][n]
+  const int64_t d = i % dim;
+  const int64_t n = (i / dim) % dstate;
+  const int64_t b = i / (dim * dstate);
+  float hv = h0 != nullptr ? h0[(b * dim + d) * dstate + n] : 0.0f;
   for (int64_t k = 0; k < K; ++k) {
     h_init[k * rows + i] = hv;
     if (k + 1 < K) hv = __builtin_fmaf(agg_p[k * rows + i], hv, agg_h[k * rows + i]);
@@ -850,13 +891,15 @@ static RowArgs<IO> row_args(const FwdArgs& a) {
   r.u = static_cast<const T*>(a.u); r.dlt = static_cast<const T*>(a.delta); r.Ag = a.A;
   r.Bg = static_cast<const T*>(a.B); r.Cg = static_cast<const T*>(a.C); r.Dg = a.D;
   r.zg = static_cast<const T*>(a.z); r.biasg = a.bias; r.yg = static_cast<T*>(a.y);
-  r.last_state = a.last_state; r.h_init = a.h_init; r.agg_p = a.agg_p; r.agg_h = a.agg_h;
+  r.last_state = a.last_state; r.h_init = a.h_init; r.h0 = a.h0; r.chunk_states = a.chunk_states;
+  r.agg_p = a.agg_p; r.agg_h = a.agg_h;
   return r;
 }
 
 static CsSizes cs_sizes(const FwdArgs& a) {
   CsSizes sz;
   sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.chunk = a.chunk; sz.softplus = a.softplus;
+  sz.state_chunk = a.chunk_states != nullptr ? a.state_chunk : 0;
   return sz;
 }
 
@@ -935,10 +978,12 @@ hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t
   return bf16 ? dispatch_mixed<BF16, kFull>(a, pairs, nchunks, st) : dispatch_mixed<F32, kFull>(a, pairs, nchunks, st);
 }
 
-hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,
-                          hipStream_t st) {
+hipError_t launch_combine(const float* agg_p, const float* agg_h, const float* h0, float* h_init, int64_t batch,
+                          int64_t dim, int64_t dstate, int64_t K, hipStream_t st) {
+  const int64_t rows = batch * dstate * dim;
   const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
-  hipLaunchKernelGGL(ssm_combine_kernel, dim3(blocks), dim3(256), 0, st, agg_p, agg_h, h_init, rows, K);
+  hipLaunchKernelGGL(ssm_combine_kernel, dim3(blocks), dim3(256), 0, st, agg_p, agg_h, h0, h_init, batch, dim, dstate,
+                     K);
   return hipGetLastError();
 }
 

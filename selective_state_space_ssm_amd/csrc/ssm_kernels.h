@@ -21,6 +21,9 @@ struct FwdArgs {
   void* y;                  // kFull
   float* last_state;        // kFull, nullable
   const float* h_init;      // kFull: [K][b][n][d] chunk start states, nullable (zero)
+  const float* h0;          // [b][d][n] start state of the sequence, nullable (zero)
+  float* chunk_states;      // kFull: [b][Ks][d][n] states at every state_chunk boundary, nullable
+  int64_t state_chunk;      // steps per chunk_states entry (multiple of the time tile)
   float* agg_p;             // kAgg: [K][b][n][d] chunk decay products
   float* agg_h;             // kAgg: [K][b][n][d] chunk end states from zero
   int64_t batch, dim, dstate, L;
@@ -32,6 +35,7 @@ struct FwdArgs {
 struct CsSizes {
   int64_t batch, dim, dstate, L;
   int64_t chunk;
+  int64_t state_chunk;   // chunk_states spacing (0: none)
   int softplus;
 };
 
@@ -44,8 +48,9 @@ hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, 
 // Mixed launch: per batch row, `pairs` blocks of two groups at S = 2 and the
 // remaining groups at S = 1 (one group per block).
 hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t nchunks, hipStream_t st);
-hipError_t launch_combine(const float* agg_p, const float* agg_h, float* h_init, int64_t rows, int64_t K,
-                          hipStream_t st);
+// h0: [batch][dim][dstate] start state or null; rows = batch*dstate*dim.
+hipError_t launch_combine(const float* agg_p, const float* agg_h, const float* h0, float* h_init, int64_t batch,
+                          int64_t dim, int64_t dstate, int64_t K, hipStream_t st);
 
 // affine_scan association-order constants and launcher
 constexpr int kAffT = 8;      // items per lane

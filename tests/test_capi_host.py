@@ -117,3 +117,17 @@ def test_plan_choice():
     assert ssm.plan_for(1, 64, 16, 256)["plan"] == "carry"
     with pytest.raises(ssm.SSMError):
         ssm.plan_for(1, 64, 17, 256)
+
+
+def test_states_entry_point_rejects_bad_state_chunk():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    args = [P(BIG), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, None, None, 0, None, P(6 * BIG),
+            P(7 * BIG), P(8 * BIG)]
+    # state_chunk must be a positive multiple of 32 when chunk_states is given
+    for sc in (0, 16, 33, -32):
+        assert lib.ssm_scan_fwd_states(*args, sc, 1, 64, 16, 256, 0, 0, None) == ssm.SSM_EINVAL
+    # chunk_states overlapping an input
+    args2 = list(args)
+    args2[12] = P(BIG)
+    assert lib.ssm_scan_fwd_states(*args2, 64, 1, 64, 16, 256, 0, 0, None) == ssm.SSM_EINVAL

@@ -153,3 +153,31 @@ def test_replay_close_to_float64_and_order_specific(oracle_lib):
     assert np.all(np.abs(ra - ea)[~normal] <= 1e-30)
     sa, sb = cpu.affine_serial_f32(a, b)
     assert not np.array_equal(sb, rb)
+
+
+def test_c_oracle_start_state_and_chunk_states(oracle_lib):
+    """The C recurrence from a given start state, with the chunk-boundary
+    states, equals the NumPy oracle's."""
+    rng = np.random.default_rng(31)
+    bsz, d, n, L, ch = 2, 5, 6, 70, 16
+    u = rng.normal(size=(bsz, d, L)).astype(np.float32)
+    dl = rng.normal(size=(bsz, d, L)).astype(np.float32)
+    z = rng.normal(size=(bsz, d, L)).astype(np.float32)
+    A = (-np.exp(rng.normal(size=(d, n)))).astype(np.float32)
+    B = rng.normal(size=(bsz, n, L)).astype(np.float32)
+    C = rng.normal(size=(bsz, n, L)).astype(np.float32)
+    D = rng.normal(size=d).astype(np.float32)
+    h0 = rng.normal(size=(bsz, d, n))
+    y_ref, last_ref, bnd_ref = ref.selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_softplus=True, h0=h0,
+                                                      chunk=ch)
+    rb, rd = np.meshgrid(np.arange(bsz), np.arange(d), indexing="ij")
+    from oracle import cpu
+    y, last, bnd = cpu.fwd_rows(u.reshape(-1, L), dl.reshape(-1, L), z.reshape(-1, L), rb.ravel(), rd.ravel(),
+                                A, B, C, D, None, True, bsz, d, n, L, h0_rows=h0.reshape(-1, n), chunk=ch)
+    K = -(-L // ch)
+    assert bnd.shape == (bsz * d, K, n)
+    assert np.max(np.abs(y.reshape(bsz, d, L) - y_ref)) <= 1e-12 * np.max(np.abs(y_ref))
+    assert np.max(np.abs(last.reshape(bsz, d, n) - last_ref)) <= 1e-12 * np.max(np.abs(last_ref))
+    # the NumPy oracle also keeps h_0 in front: its entries 1..K are the C oracle's 0..K-1
+    got = bnd.reshape(bsz, d, K, n).transpose(0, 1, 3, 2)
+    assert np.max(np.abs(got - bnd_ref[..., 1:])) <= 1e-12 * np.max(np.abs(bnd_ref))

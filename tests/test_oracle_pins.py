@@ -344,3 +344,48 @@ def test_chunk_state_sizes_printed_on_page():
     _, _, bnd = ref.selective_scan_fwd(u, dl, -np.ones((d, n)), rng.normal(size=(bsz, n, L)),
                                        rng.normal(size=(bsz, n, L)), delta_softplus=True, chunk=ch)
     assert bnd.shape == (bsz, d, n, L // ch + 1)
+
+
+# ---------------------------------------------------------------- start state
+
+def test_start_state_decays_in_closed_form():
+    """With no input (B = 0) the state only decays: h_t = exp(A * sum_{s<=t}
+    Delta_s) * h_0, the h_t = A_t h_0 + B_t form of [Scan page] §2.1 with
+    B_t = 0, written here as one exponential of the running sum; y follows as
+    C_t . h_t + D u_t."""
+    rng = np.random.default_rng(21)
+    bsz, d, n, L = 2, 3, 4, 40
+    u = rng.normal(size=(bsz, d, L))
+    dl = rng.normal(size=(bsz, d, L))
+    A = -np.exp(rng.normal(size=(d, n)))
+    C = rng.normal(size=(bsz, n, L))
+    D = rng.normal(size=d)
+    h0 = rng.normal(size=(bsz, d, n))
+    y, last = ref.selective_scan_fwd(u, dl, A, np.zeros((bsz, n, L)), C, D=D, delta_softplus=True, h0=h0)
+    dt = ref.softplus(dl)
+    cum = np.cumsum(dt, axis=-1)                                        # [b, d, L]
+    h = np.exp(cum[:, :, None, :] * A[None, :, :, None]) * h0[..., None]  # [b, d, n, L]
+    y_cf = np.einsum("bdnt,bnt->bdt", h, C) + D[None, :, None] * u
+    assert np.max(np.abs(y - y_cf)) <= 1e-12 * np.max(np.abs(y_cf))
+    assert np.max(np.abs(last - h[..., -1])) <= 1e-12 * np.max(np.abs(h[..., -1]))
+
+
+def test_start_state_split_invariance():
+    """Running steps [0, t1) and then [t1, L) from the state reached gives the
+    whole run: the recurrence composes (h_t = A_t h_0 + B_t for any h_0,
+    [Scan page] §2.1).  A dropped or misplaced h0 term fails this."""
+    rng = np.random.default_rng(22)
+    bsz, d, n, L, t1 = 2, 3, 5, 30, 11
+    u = rng.normal(size=(bsz, d, L)); dl = rng.normal(size=(bsz, d, L)); z = rng.normal(size=(bsz, d, L))
+    A = -np.exp(rng.normal(size=(d, n)))
+    B = rng.normal(size=(bsz, n, L)); C = rng.normal(size=(bsz, n, L))
+    D = rng.normal(size=d); bias = rng.normal(size=d)
+    h0 = rng.normal(size=(bsz, d, n))
+    kw = dict(D=D, delta_bias=bias, delta_softplus=True)
+    y, last = ref.selective_scan_fwd(u, dl, A, B, C, z=z, h0=h0, **kw)
+    y1, h1 = ref.selective_scan_fwd(u[..., :t1], dl[..., :t1], A, B[..., :t1], C[..., :t1], z=z[..., :t1],
+                                    h0=h0, **kw)
+    y2, h2 = ref.selective_scan_fwd(u[..., t1:], dl[..., t1:], A, B[..., t1:], C[..., t1:], z=z[..., t1:],
+                                    h0=h1, **kw)
+    assert np.max(np.abs(np.concatenate([y1, y2], axis=-1) - y)) <= 1e-13 * np.max(np.abs(y))
+    assert np.max(np.abs(h2 - last)) <= 1e-13 * np.max(np.abs(last))
