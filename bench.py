@@ -57,6 +57,9 @@ def parse():
                    help="start every channel from a random state (ssm_scan_fwd_states)")
     p.add_argument("--state-chunk", type=int, default=0,
                    help="also write the state every STATE_CHUNK steps (ssm_scan_fwd_states)")
+    p.add_argument("--decode", type=int, default=0, metavar="BATCH",
+                   help="time ssm_step (one recurrent decode step) for BATCH sequences of the workload's "
+                        "layer shape instead of the scan")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -121,6 +124,52 @@ def calibrate_copy(args):
           flush=True)
 
 
+def decode_bench(args):
+    """One ssm_step per timed step for args.decode sequences of the
+    workload's layer shape; reports GB/s of the state read and write plus the
+    step's inputs and outputs (algorithmic bytes)."""
+    import torch
+    import selective_state_space_ssm_amd as ssm
+    import workloads
+    dev = torch.device("cuda:0")
+    w0 = workloads.WORKLOADS[args.workload]
+    w = w0.with_sizes(batch=args.decode, L=1)
+    inp = workloads.make_inputs(w, device=dev, seed=0)
+    pick = lambda x: None if x is None else x[..., 0].contiguous()
+    u, dl, z, B, C = (pick(inp[k]) for k in ("u", "delta", "z", "B", "C"))
+    state = torch.randn((w.batch, w.dim, w.dstate), device=dev)
+    y = torch.empty_like(u)
+
+    def step():
+        ssm.ssm_step(u, dl, inp["A"], B, C, state, D=inp["D"], z=z, delta_bias=inp["delta_bias"],
+                     delta_softplus=w.softplus, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    es = 4 if w.dtype == "f32" else 2
+    nbd = w.batch * w.dim
+    bytes_alg = (8 * nbd * w.dstate + nbd * es * (3 + int(w.gated)) + 2 * w.batch * w.dstate * es
+                 + 4 * w.dim * w.dstate + 8 * w.dim)
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
+                      "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+                      "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)", "data": "synthetic",
+                      "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
+                                 "d_state": w.dstate, "io_dtype": w.dtype},
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg}), flush=True)
+
+
 def cpu_baseline(inp, w, budget_s):
     """The float64 C oracle, as it is, on a bounded sample of whole channels
     of the same workload; throughput scaled to the workload's GB/s."""
@@ -166,6 +215,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args)
+        return
+    if args.decode:
+        decode_bench(args)
         return
     import torch
 

@@ -154,6 +154,29 @@ int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L
                       int *plan, int *states_per_lane, int64_t *chunk);
 
 /*
+ * ssm_step -- one recurrent step of the selective scan for every (batch,
+ * channel): the constant-time inference form of the recurrence
+ * ([Mamba-2 page] §7; the step itself is [Scan page] §1.2):
+ *     x     = delta[b,d] + delta_bias[d];  Delta = softplus(x) or x
+ *     h_n   = exp(Delta * A[d,n]) * h_n + Delta * B[b,n] * u[b,d]
+ *     y     = sum_n C[b,n] * h_n + D[d] * u[b,d];  y *= silu(z[b,d])
+ * i.e. one step t of ssm_scan_fwd with h taken from state_in.
+ *   u, delta, z : [batch, d_inner], dtype `dtype`; z nullable (no gate).
+ *   A           : [d_inner, d_state] float32.
+ *   B, C        : [batch, d_state], dtype `dtype`.
+ *   D, delta_bias : [d_inner] float32, nullable.
+ *   state_in    : [batch, d_inner, d_state] float32, the state before the step.
+ *   state_out   : [batch, d_inner, d_state] float32, the state after the step;
+ *                 may equal state_in (updated in place) or be disjoint from it.
+ *   y           : [batch, d_inner], dtype `dtype`, output.
+ * Errors as ssm_scan_fwd (d_state <= 16).
+ */
+int ssm_step(const void *u, const void *delta, const float *A, const void *B, const void *C,
+             const float *D, const void *z, const float *delta_bias, int delta_softplus,
+             const float *state_in, float *state_out, void *y,
+             int64_t batch, int64_t d_inner, int64_t d_state, int dtype, void *stream);
+
+/*
  * affine_scan -- inclusive scan of affine pairs along each row
  * ([Scan page] §1.2 and §2.1; [Mamba-2 page] §2.2).
  * A pair (a, b) is the map h -> a*h + b; composition, later step first, is

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,8 @@ def load_library():
     lib.ssm_scan_fwd_plan.restype = I
     lib.ssm_scan_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_fwd_states.restype = I
+    lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I, P]
+    lib.ssm_step.restype = I
     lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
                                       ctypes.POINTER(I64)]
     lib.ssm_scan_plan_for.restype = I
@@ -215,6 +217,55 @@ def ssm_scan_fwd_states(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B
                                      SSM_F32 if dt == torch.float32 else SSM_BF16, PLANS[plan], _stream(device))
     _check(rc)
     return y, last_state, chunk_states
+
+
+def ssm_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             state: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+             state_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+    """One recurrent step (see ``ssm_step`` in include/ssm_scan.h).
+
+    u, delta, z: [b, d]; B, C: [b, n]; A: [d, n] float32; state: [b, d, n]
+    float32.  The new state goes to ``state_out`` (default: ``state`` itself,
+    updated in place).  Returns (y [b, d], state_out).
+    """
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError("ssm_step needs CUDA/HIP tensors")
+    if u.dim() != 2 or A.dim() != 2:
+        raise ValueError("u must be [b, d] and A [d, n]")
+    bsz, dim = u.shape
+    n = A.shape[1]
+    dt = u.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    _need(u, "u", dt, device, (bsz, dim))
+    _need(delta, "delta", dt, device, (bsz, dim))
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(B, "B", dt, device, (bsz, n))
+    _need(C, "C", dt, device, (bsz, n))
+    _need(state, "state", torch.float32, device, (bsz, dim, n))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim))
+    if D is not None:
+        _need(D, "D", torch.float32, device, (dim,))
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", torch.float32, device, (dim,))
+    if state_out is None:
+        state_out = state
+    else:
+        _need(state_out, "state_out", torch.float32, device, (bsz, dim, n))
+    if y is None:
+        y = torch.empty_like(u)
+    else:
+        _need(y, "y", dt, device, (bsz, dim))
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_step(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                          int(bool(delta_softplus)), _ptr(state), _ptr(state_out), _ptr(y), bsz, dim, n,
+                          SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
+    _check(rc)
+    return y, state_out
 
 
 def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,

@@ -259,6 +259,41 @@ int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L
   return SSM_OK;
 }
 
+int ssm_step(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+             const void* z, const float* delta_bias, int delta_softplus, const float* state_in, float* state_out,
+             void* y, int64_t batch, int64_t d_inner, int64_t d_state, int dtype, void* stream) {
+  g_err.clear();
+  if (!u || !delta || !A || !B || !C || !state_in || !state_out || !y)
+    return fail(SSM_EINVAL, "u, delta, A, B, C, state_in, state_out and y must not be NULL");
+  if (int rc = check_sizes(batch, d_inner, d_state, 1)) return rc;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, state_in, state_out, y};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const uint64_t es = dtype == SSM_F32 ? 4 : 2;
+  const uint64_t nbd = uint64_t(batch) * d_inner, nbn = uint64_t(batch) * d_state;
+  const uint64_t nstate = nbd * d_state;
+  const Range rin[] = {range_of(u, nbd * es), range_of(delta, nbd * es), range_of(z, nbd * es),
+                       range_of(B, nbn * es), range_of(C, nbn * es), range_of(A, uint64_t(d_inner) * d_state * 4),
+                       range_of(D, uint64_t(d_inner) * 4), range_of(delta_bias, uint64_t(d_inner) * 4)};
+  const Range ry = range_of(y, nbd * es);
+  const Range rsi = range_of(state_in, nstate * 4), rso = range_of(state_out, nstate * 4);
+  for (const Range& r : rin)
+    if (overlap(ry, r) || overlap(rso, r) || overlap(rsi, r))
+      return fail(SSM_EINVAL, "y, state_in and state_out must not overlap the other inputs");
+  if (overlap(ry, rso) || overlap(ry, rsi)) return fail(SSM_EINVAL, "y overlaps the state");
+  if (state_in != state_out && overlap(rsi, rso))
+    return fail(SSM_EINVAL, "state_out must equal state_in or be disjoint from it");
+  ssm::StepArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.state_in = state_in; a.state_out = state_out; a.y = y;
+  a.batch = batch; a.dim = d_inner; a.dstate = d_state; a.softplus = delta_softplus;
+  hipError_t e = ssm::launch_step(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "recurrent step launch");
+  return SSM_OK;
+}
+
 int affine_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t rows, int64_t L,
                 void* stream) {
   g_err.clear();

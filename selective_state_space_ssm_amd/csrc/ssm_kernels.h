@@ -52,6 +52,24 @@ hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t
 hipError_t launch_combine(const float* agg_p, const float* agg_h, const float* h0, float* h_init, int64_t batch,
                           int64_t dim, int64_t dstate, int64_t K, hipStream_t st);
 
+// One recurrent step (decode) for every (batch, channel).
+struct StepArgs {
+  const void* u;        // [b][d]
+  const void* delta;    // [b][d]
+  const float* A;       // [d][n]
+  const void* B;        // [b][n]
+  const void* C;        // [b][n]
+  const float* D;       // [d] nullable
+  const void* z;        // [b][d] nullable
+  const float* bias;    // [d] nullable
+  const float* state_in;  // [b][d][n]
+  float* state_out;       // [b][d][n], may equal state_in
+  void* y;              // [b][d]
+  int64_t batch, dim, dstate;
+  int softplus;
+};
+hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
+
 // affine_scan association-order constants and launcher
 constexpr int kAffT = 8;      // items per lane
 constexpr int kAffLanes = 64; // lanes per wave

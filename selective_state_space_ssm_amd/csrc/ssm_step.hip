@@ -1,0 +1,153 @@
+// One recurrent step of the selective scan for every (batch, channel) on
+// gfx950: the decode-time form of the recurrence ([Mamba-2 page]
+// "Mamba (part 2): parallel scan and hardware-aware optimisation", §7 on
+// constant-time recurrent inference; [Scan page] "Hardware-aware parallel
+// associative scan for Mamba", §1.2 for the step itself):
+//     Delta = softplus(delta + bias) (or delta + bias)
+//     h_n   = exp(Delta * A[d,n]) * h_n + Delta * B[b,n] * u
+//     y     = sum_n C[b,n] * h_n + D[d] * u,   y *= silu(z)
+//
+// Layout and mapping: the state is [b][d][n] float32.  Each channel owns four
+// consecutive lanes (a DPP quad); lane q of the quad carries states
+// [4q, 4q+4) as one float4, so a wave covers 16 channels and every state
+// load and store is a coalesced 16-byte access.  The four partial sums of
+// C . h meet by two DPP quad permutations; lane 0 of the quad stores y.
+// The step is bound by the state's HBM traffic (read and write 8*n bytes
+// per channel); Delta and the gate are recomputed by the four lanes of a
+// quad, which costs nothing next to that.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_kernels.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct F32S {
+  using T = float;
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+
+struct BF16S {
+  using T = uint16_t;
+  static __device__ __forceinline__ float ld(const uint16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) {
+    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+  }
+};
+
+// quad_perm DPP controls: swap neighbours, swap pairs
+constexpr int kQuadSwap1 = 0xB1;  // [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;  // [2, 3, 0, 1]
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xf, 0xf, false));
+  return v;
+}
+
+}  // namespace
+
+// Grid: one thread per (channel, quad), 256 threads (64 channels) per block.
+// VEC4: d_state is a multiple of 4 (float4 state and B/C accesses).
+template <typename IO, bool VEC4>
+__global__ __launch_bounds__(256) void ssm_step_kernel(
+    const typename IO::T* __restrict__ u, const typename IO::T* __restrict__ dlt, const float* __restrict__ A,
+    const typename IO::T* __restrict__ B, const typename IO::T* __restrict__ C, const float* __restrict__ D,
+    const typename IO::T* __restrict__ z, const float* __restrict__ bias, const float* state_in,
+    float* state_out, typename IO::T* __restrict__ y, int64_t batch, int64_t dim, int64_t N, int softplus) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t ch = gid >> 2;  // (b, d) flattened, d fastest
+  const int q = static_cast<int>(gid & 3);
+  const bool valid = ch < batch * dim;
+  const int64_t chc = valid ? ch : 0;
+  const int64_t b = chc / dim;
+  const int64_t d = chc - b * dim;
+
+  const float uu = IO::ld(u + chc);
+  const float x = IO::ld(dlt + chc) + (bias != nullptr ? bias[d] : 0.0f);
+  float dt = x;
+  if (softplus) {
+    // softplus(x) = log(1 + e^x), computed as ln2 * log2(1 + 2^(x log2 e));
+    // x itself above 44 (where e^-x is below float32 resolution)
+    const float sp = 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e));
+    dt = x > 44.0f ? x : sp;
+  }
+  const float dtu = dt * uu;
+  const float dt2 = dt * kLog2e;
+
+  float part = 0.0f;
+  const int64_t n0 = 4 * q;
+  if (valid && n0 < N) {
+    const int64_t so = ch * N + n0;
+    float h[4], bv[4], cv[4], av[4];
+    if constexpr (VEC4) {
+      const float4 hs = *reinterpret_cast<const float4*>(state_in + so);
+      const float4 as = *reinterpret_cast<const float4*>(A + d * N + n0);
+      h[0] = hs.x; h[1] = hs.y; h[2] = hs.z; h[3] = hs.w;
+      av[0] = as.x; av[1] = as.y; av[2] = as.z; av[3] = as.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bv[e] = IO::ld(B + b * N + n0 + e);
+        cv[e] = IO::ld(C + b * N + n0 + e);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = n0 + e < N;
+        h[e] = ok ? state_in[so + e] : 0.0f;
+        av[e] = ok ? A[d * N + n0 + e] : 0.0f;
+        bv[e] = ok ? IO::ld(B + b * N + n0 + e) : 0.0f;
+        cv[e] = ok ? IO::ld(C + b * N + n0 + e) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt2 * av[e]), h[e], dtu * bv[e]);
+      part = __builtin_fmaf(cv[e], h[e], part);
+    }
+    if constexpr (VEC4) {
+      *reinterpret_cast<float4*>(state_out + so) = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n0 + e < N) state_out[so + e] = h[e];
+    }
+  }
+  const float tot = quad_sum(part);
+  if (valid && q == 0) {
+    float yv = tot + (D != nullptr ? D[d] : 0.0f) * uu;
+    if (z != nullptr) {
+      const float zz = IO::ld(z + chc);
+      yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * zz));
+    }
+    IO::st(y + chc, yv);
+  }
+}
+
+template <typename IO>
+static hipError_t launch_step_t(const StepArgs& a, hipStream_t st) {
+  using T = typename IO::T;
+  const int64_t threads = a.batch * a.dim * 4;
+  const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, static_cast<const T*>(a.u),
+                       static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
+                       a.D, static_cast<const T*>(a.z), a.bias, a.state_in, a.state_out, static_cast<T*>(a.y),
+                       a.batch, a.dim, a.dstate, a.softplus);
+    return hipGetLastError();
+  };
+  if (a.dstate % 4 == 0) return run(ssm_step_kernel<IO, true>);
+  return run(ssm_step_kernel<IO, false>);
+}
+
+hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st) {
+  return bf16 ? launch_step_t<BF16S>(a, st) : launch_step_t<F32S>(a, st);
+}
+
+}  // namespace ssm

@@ -131,3 +131,20 @@ def test_states_entry_point_rejects_bad_state_chunk():
     args2 = list(args)
     args2[12] = P(BIG)
     assert lib.ssm_scan_fwd_states(*args2, 64, 1, 64, 16, 256, 0, 0, None) == ssm.SSM_EINVAL
+
+
+def test_step_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    base = [P(BIG), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, None, None, 0, P(6 * BIG), P(6 * BIG),
+            P(7 * BIG)]
+    ok_sizes = (8, 64, 16, 0, None)
+    bad = list(base); bad[0] = None
+    assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # null u
+    assert lib.ssm_step(*base, 8, 64, 17, 0, None) == ssm.SSM_EUNSUPPORTED      # d_state > 16
+    bad = list(base); bad[10] = P(6 * BIG + 16)
+    assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # partial state overlap
+    bad = list(base); bad[11] = P(6 * BIG)
+    assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # y on the state
+    bad = list(base); bad[8] = 3
+    assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # softplus flag
