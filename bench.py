@@ -74,25 +74,28 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # same counter to the known byte count of a plain device copy (bench.py
 # --calibrate-copy).  Keyed by workload; valid only for the kernel sources
 # whose digest is stored with it (any change to them makes the figure stale,
-# and it is reported as null).  The summaries these come from are the
-# profiles/*counters*.md files.
+# and it is reported as null).  Each entry names the profile summary the
+# counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "c1731531534fdaad", "plan": "mixed", "fetch_bytes": 334083491, "write_bytes": 101454738,
+    "130m": {"digest": "174208ac40b28545", "plan": "mixed", "fetch_bytes": 333303382, "write_bytes": 101457170,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
+    "1.4b": {"digest": "174208ac40b28545", "plan": "carry", "fetch_bytes": 438892668, "write_bytes": 167044617,
+             "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
 }
 
 
 def kernel_digest() -> str:
-    """sha256 over the HIP sources and build flags of the library."""
+    """sha256 over the source of the forward scan kernels and the compiler
+    flags they are built with: a stored traffic figure holds only for the
+    build it was counted on."""
     import hashlib
     pkg = os.path.join(ROOT, "selective_state_space_ssm_amd")
+    sys.path.insert(0, ROOT)
+    from selective_state_space_ssm_amd import build as _b
     h = hashlib.sha256()
-    for sub in ("csrc", ""):
-        d = os.path.join(pkg, sub)
-        for name in sorted(os.listdir(d)):
-            if name.endswith((".hip", ".h", ".cpp")) or name == "build.py":
-                with open(os.path.join(d, name), "rb") as f:
-                    h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(pkg, "csrc", "ssm_fwd.hip"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(_b.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
