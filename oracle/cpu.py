@@ -30,6 +30,9 @@ def lib():
         L.ssm_oracle_fwd_rows_h0.argtypes = [P, P, P, P, P, I64, P, P, P, P, P, ctypes.c_int,
                                              I64, I64, I64, I64, P, I64, P, P, P, ctypes.c_int]
         L.ssm_oracle_fwd_rows_h0.restype = ctypes.c_int
+        L.ssm_oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, I64, I64, I64, I64,
+                                     P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        L.ssm_oracle_bwd.restype = ctypes.c_int
         L.affine_scan_serial_f32.argtypes = [P, P, P, P, I64, I64]
         L.affine_scan_serial_f32.restype = None
         L.affine_scan_replay_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -94,6 +97,31 @@ def fwd_full(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
                        None if z is None else z.reshape(bsz * dim, L), rb.ravel(), rd.ravel(),
                        A, B, C, D, delta_bias, delta_softplus, bsz, dim, dstate, L, nthreads=nthreads)
     return y.reshape(bsz, dim, L), last.reshape(bsz, dim, dstate)
+
+
+def bwd_full(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+             h0=None, dy=None, dlast=None, nthreads=0):
+    """float64 gradients of the whole [b, d, L] problem (ref_cpu.c
+    ssm_oracle_bwd).  Inputs are taken at their float32 values (bfloat16
+    tensors upcast exactly).  Returns a dict like oracle.ref.selective_scan_bwd:
+    du, ddelta, dz (None without z) [b,d,L]; dA [d,n]; dB, dC [b,n,L];
+    dD, ddelta_bias [d]; dh0 [b,d,n]."""
+    u = _f32(u); delta = _f32(delta); z = _f32(z); A = _f32(A); B = _f32(B); C = _f32(C)
+    D = _f32(D); delta_bias = _f32(delta_bias); h0 = _f32(h0); dy = _f32(dy); dlast = _f32(dlast)
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    out = {k: np.empty(sh, dtype=np.float64) for k, sh in
+           (("du", (bsz, dim, L)), ("ddelta", (bsz, dim, L)), ("dA", (dim, n)), ("dB", (bsz, n, L)),
+            ("dC", (bsz, n, L)), ("dD", (dim,)), ("ddelta_bias", (dim,)), ("dh0", (bsz, dim, n)))}
+    out["dz"] = np.empty((bsz, dim, L), dtype=np.float64) if z is not None else None
+    rc = lib().ssm_oracle_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                              int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dlast), bsz, dim, n, L,
+                              _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+                              int(nthreads))
+    if rc != 0:
+        raise ValueError("ssm_oracle_bwd rejected its arguments")
+    return out
 
 
 def affine_serial_f32(a, b):

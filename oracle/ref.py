@@ -53,6 +53,7 @@ __all__ = [
     "silu",
     "selective_scan_fwd",
     "selective_scan_bruteforce",
+    "selective_scan_bwd",
     "affine_scan",
     "lti_closed_form",
 ]
@@ -363,6 +364,89 @@ def selective_scan_bruteforce(u, delta, A, B, C, D=None, z=None, delta_bias=None
                     acc *= float(silu(z[bi, di, t]))
                 y[bi, di, t] = acc
     return y, last
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=False, h0=None, dy=None, dlast=None):
+    """Gradients of the selective scan, float64, by reverse-mode chain rule.
+
+    The forward pass is the one of ``selective_scan_fwd``; the loss is
+    sum(dy * y) + sum(dlast * last_state), i.e. dy and dlast are the incoming
+    gradients of y [b,d,L] and of the final state [b,d,n] (either may be
+    None: zero).  The states h_t are kept for every step (this is the plain
+    definition; the chunked recomputation of [Scan page] §4.2 and the
+    Mamba-2 page §4.3 reaches the same values with only chunk-boundary
+    states stored).
+
+    With s_t the sum before the gate (s_t = C_t . h_t + D u_t, y_t = s_t *
+    silu(z_t)) and g_t = dL/dh_t:
+
+        gs_t   = dy_t * silu(z_t)                (dy_t without a gate)
+        dz_t   = dy_t * s_t * silu'(z_t),  silu'(z) = sig(z) (1 + z (1 - sig(z)))
+        g_t    = C_t gs_t + a_{t+1} g_{t+1},  starting from g_L = dlast
+        dC_t  += gs_t h_t                        (summed over channels d)
+        dB_t  += g_t Delta_t u_t                 (summed over channels d)
+        du_t   = D gs_t + Delta_t sum_n g_t B_t
+        dDelta = sum_n g_t (A a_t h_{t-1} + B_t u_t)
+        dA    += g_t a_t h_{t-1} Delta_t         (summed over b and t)
+        dD    += gs_t u_t                        (summed over b and t)
+        dx_t   = dDelta_t * sig(x_t) with softplus (softplus' = sigmoid),
+                 else dDelta_t;  ddelta_t = dx_t,  ddelta_bias += dx_t
+        dh0    = a_0 g_0
+
+    where h_{-1} is h0 (zero by default).  Returns a dict with keys du,
+    ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0 (dz None without a gate;
+    dD and ddelta_bias are computed whether or not D and delta_bias are
+    given, as the gradients at zero).
+    """
+    u = _f64(u); delta = _f64(delta); A = _f64(A); B = _f64(B); C = _f64(C)
+    D = _f64(D); z = _f64(z); delta_bias = _f64(delta_bias)
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    dy = np.zeros((bsz, dim, L)) if dy is None else _f64(dy)
+    dlast = np.zeros((bsz, dim, n)) if dlast is None else _f64(dlast)
+    x = delta + (delta_bias[None, :, None] if delta_bias is not None else 0.0)
+    dt = softplus(x) if delta_softplus else x
+    Dv = np.zeros(dim) if D is None else D
+    # forward, keeping every state: hs[t+1] = h_t, hs[0] = h0
+    hs = np.empty((L + 1, bsz, dim, n))
+    hs[0] = 0.0 if h0 is None else _f64(h0)
+    aa = np.empty((L, bsz, dim, n))
+    s = np.empty((bsz, dim, L))
+    for t in range(L):
+        aa[t] = np.exp(dt[:, :, t, None] * A[None, :, :])
+        bb = dt[:, :, t, None] * B[:, None, :, t] * u[:, :, t, None]
+        hs[t + 1] = aa[t] * hs[t] + bb
+        s[:, :, t] = np.einsum("bdn,bn->bd", hs[t + 1], C[:, :, t]) + Dv[None, :] * u[:, :, t]
+    if z is not None:
+        sig = 1.0 / (1.0 + np.exp(-z))
+        gs = dy * z * sig
+        dz = dy * s * sig * (1.0 + z * (1.0 - sig))
+    else:
+        gs = dy
+        dz = None
+    du = np.empty((bsz, dim, L))
+    ddt = np.empty((bsz, dim, L))
+    dA = np.zeros((dim, n))
+    dB = np.zeros((bsz, n, L))
+    dC = np.zeros((bsz, n, L))
+    g = dlast.copy()
+    a_next = np.ones((bsz, dim, n))
+    for t in range(L - 1, -1, -1):
+        g = C[:, None, :, t] * gs[:, :, t, None] + a_next * g
+        h_prev = hs[t]
+        dC[:, :, t] = np.einsum("bd,bdn->bn", gs[:, :, t], hs[t + 1])
+        dB[:, :, t] = np.einsum("bdn,bd->bn", g, dt[:, :, t] * u[:, :, t])
+        du[:, :, t] = Dv[None, :] * gs[:, :, t] + dt[:, :, t] * np.einsum("bdn,bn->bd", g, B[:, :, t])
+        ga = g * aa[t] * h_prev
+        ddt[:, :, t] = np.einsum("bdn,dn->bd", ga, A) + u[:, :, t] * np.einsum("bdn,bn->bd", g, B[:, :, t])
+        dA += np.einsum("bdn,bd->dn", ga, dt[:, :, t])
+        a_next = aa[t]
+    dh0 = aa[0] * g if L > 0 else g
+    dD = np.einsum("bdl,bdl->d", gs, u)
+    dx = ddt * (1.0 / (1.0 + np.exp(-x))) if delta_softplus else ddt
+    return {"du": du, "ddelta": dx, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz,
+            "ddelta_bias": dx.sum(axis=(0, 2)), "dh0": dh0}
 
 
 def lti_closed_form(a: float, b):

@@ -129,6 +129,159 @@ int ssm_oracle_fwd_rows_h0(const float *u_rows, const float *delta_rows, const f
 }
 
 /*
+ * Gradients of the selective scan (reverse-mode chain rule of the forward
+ * above), float64, for the whole [batch, dim, L] problem.  The loss is
+ * sum(dy * y) + sum(dlast * last_state); dlast and h0 may be NULL (zero).
+ * Per (batch, channel) chain the forward is run keeping every state, then
+ * the steps are walked back ([Scan page] §4.2 and [Mamba-2 page] §4.3
+ * recompute the same states chunk by chunk; here all are kept):
+ *     gs = dy*silu(z) (dy without gate);  dz = dy*s*silu'(z), s = C.h + D u
+ *     g_t = C_t gs_t + a_{t+1} g_{t+1}  (g after the last step = dlast)
+ *     dC[b,n,t] += gs_t h_t[n];  dB[b,n,t] += g_t[n] dt_t u_t
+ *     du_t = D gs_t + dt_t sum_n g_t[n] B[b,n,t]
+ *     ddt_t = sum_n g_t[n] (A[d,n] a_t[n] h_{t-1}[n] + B[b,n,t] u_t)
+ *     dA[d,n] += g_t[n] a_t[n] h_{t-1}[n] dt_t;  dD[d] += gs_t u_t
+ *     ddelta_t = ddt_t * sigmoid(x_t) with softplus, else ddt_t
+ *     ddelta_bias[d] += ddelta_t;  dh0 = a_0 g_0
+ * Outputs (all float64, all required except dz, which is required iff z is
+ * given): du, ddelta, dz [b,d,L]; dA [d,n]; dB, dC [b,n,L]; dD, dbias [d];
+ * dh0 [b,d,n].  Channels run in parallel (OpenMP, static); the sums over
+ * channels (dB, dC) go through per-thread buffers added in thread order.
+ * Returns 0, or 1 on a bad argument or allocation failure.
+ */
+int ssm_oracle_bwd(const float *u, const float *delta, const float *A, const float *B, const float *C,
+                   const float *D, const float *z, const float *delta_bias, int delta_softplus,
+                   const float *h0, const float *dy, const float *dlast,
+                   int64_t batch, int64_t dim, int64_t dstate, int64_t L,
+                   double *du, double *ddelta, double *dz, double *dA, double *dB, double *dC,
+                   double *dD, double *dbias, double *dh0, int nthreads) {
+    if (!u || !delta || !A || !B || !C || !dy) return 1;
+    if (!du || !ddelta || !dA || !dB || !dC || !dD || !dbias || !dh0) return 1;
+    if ((z != NULL) != (dz != NULL)) return 1;
+    if (batch <= 0 || dim <= 0 || dstate <= 0 || L <= 0) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int maxth = omp_get_max_threads();
+#else
+    (void)nthreads;
+    const int maxth = 1;
+#endif
+    const size_t bcn = (size_t)(batch * dstate * L);
+    double *partB = (double *)calloc((size_t)maxth * bcn, sizeof(double));
+    double *partC = (double *)calloc((size_t)maxth * bcn, sizeof(double));
+    if (!partB || !partC) { free(partB); free(partC); return 1; }
+    int bad = 0, nth_used = 1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#pragma omp single
+        nth_used = omp_get_num_threads();
+#else
+        const int tid = 0;
+#endif
+        double *pB = partB + (size_t)tid * bcn;
+        double *pC = partC + (size_t)tid * bcn;
+        double *hs = (double *)malloc((size_t)(L + 1) * (size_t)dstate * sizeof(double));
+        double *aa = (double *)malloc((size_t)L * (size_t)dstate * sizeof(double));
+        double *dts = (double *)malloc((size_t)L * sizeof(double));
+        double *gss = (double *)malloc((size_t)L * sizeof(double));
+        double *g = (double *)malloc((size_t)dstate * sizeof(double));
+        if (!hs || !aa || !dts || !gss || !g) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t d = 0; d < dim; ++d) {
+            if (!hs || !aa || !dts || !gss || !g) continue;
+            const double bias = delta_bias ? (double)delta_bias[d] : 0.0;
+            const double Dd = D ? (double)D[d] : 0.0;
+            double sumD = 0.0, sumBias = 0.0;
+            for (int64_t n = 0; n < dstate; ++n) dA[d * dstate + n] = 0.0;
+            for (int64_t b = 0; b < batch; ++b) {
+                const int64_t row = (b * dim + d) * L;
+                /* forward, keeping h_t for every t (hs[t+1]) and a_t */
+                for (int64_t n = 0; n < dstate; ++n)
+                    hs[n] = h0 ? (double)h0[(b * dim + d) * dstate + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const double uu = (double)u[row + t];
+                    const double x = (double)delta[row + t] + bias;
+                    const double dt = delta_softplus ? softplus_d(x) : x;
+                    dts[t] = dt;
+                    double s = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const double a = exp(dt * (double)A[d * dstate + n]);
+                        aa[t * dstate + n] = a;
+                        const double hn = a * hs[t * dstate + n] + dt * (double)B[(b * dstate + n) * L + t] * uu;
+                        hs[(t + 1) * dstate + n] = hn;
+                        s += (double)C[(b * dstate + n) * L + t] * hn;
+                    }
+                    s += Dd * uu;
+                    const double gy = (double)dy[row + t];
+                    if (z) {
+                        const double zz = (double)z[row + t];
+                        const double sg = 1.0 / (1.0 + exp(-zz));
+                        gss[t] = gy * zz * sg;
+                        dz[row + t] = gy * s * sg * (1.0 + zz * (1.0 - sg));
+                    } else {
+                        gss[t] = gy;
+                    }
+                }
+                /* reverse */
+                for (int64_t n = 0; n < dstate; ++n)
+                    g[n] = dlast ? (double)dlast[(b * dim + d) * dstate + n] : 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    const double uu = (double)u[row + t];
+                    const double dt = dts[t];
+                    const double gs = gss[t];
+                    double r = 0.0, w = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const double a_next = (t + 1 < L) ? aa[(t + 1) * dstate + n] : 1.0;
+                        const double Bv = (double)B[(b * dstate + n) * L + t];
+                        const double Cv = (double)C[(b * dstate + n) * L + t];
+                        g[n] = Cv * gs + a_next * g[n];
+                        pC[(b * dstate + n) * L + t] += gs * hs[(t + 1) * dstate + n];
+                        pB[(b * dstate + n) * L + t] += g[n] * dt * uu;
+                        r += g[n] * Bv;
+                        const double ga = g[n] * aa[t * dstate + n] * hs[t * dstate + n];
+                        w += ga * (double)A[d * dstate + n];
+                        dA[d * dstate + n] += ga * dt;
+                    }
+                    du[row + t] = Dd * gs + dt * r;
+                    const double ddt = w + uu * r;
+                    double dd = ddt;
+                    if (delta_softplus) {
+                        const double x = (double)delta[row + t] + bias;
+                        dd = ddt / (1.0 + exp(-x));
+                    }
+                    ddelta[row + t] = dd;
+                    sumBias += dd;
+                    sumD += gs * uu;
+                }
+                for (int64_t n = 0; n < dstate; ++n)
+                    dh0[(b * dim + d) * dstate + n] = aa[n] * g[n];
+            }
+            dD[d] = sumD;
+            dbias[d] = sumBias;
+        }
+        free(hs); free(aa); free(dts); free(gss); free(g);
+    }
+    if (!bad) {
+        for (size_t i = 0; i < bcn; ++i) {
+            double sb = 0.0, sc = 0.0;
+            for (int th = 0; th < nth_used; ++th) {
+                sb += partB[(size_t)th * bcn + i];
+                sc += partC[(size_t)th * bcn + i];
+            }
+            dB[i] = sb;
+            dC[i] = sc;
+        }
+    }
+    free(partB); free(partC);
+    return bad ? 1 : 0;
+}
+
+/*
  * Serial float32 left fold with an explicit fused multiply-add:
  *     A_t = a_t * A_{t-1},  H_t = fmaf(a_t, H_{t-1}, b_t),  (A, H) from (1, 0).
  * This is the plain serial order of the recurrence in [Scan page] §2.1.
