@@ -77,9 +77,9 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "174208ac40b28545", "plan": "mixed", "fetch_bytes": 333303382, "write_bytes": 101457170,
+    "130m": {"digest": "724da264406c7a1c", "plan": "mixed", "fetch_bytes": 333303382, "write_bytes": 101457170,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "174208ac40b28545", "plan": "carry", "fetch_bytes": 438892668, "write_bytes": 167044617,
+    "1.4b": {"digest": "724da264406c7a1c", "plan": "carry", "fetch_bytes": 438892668, "write_bytes": 167044617,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
 }
 
@@ -93,8 +93,9 @@ def kernel_digest() -> str:
     sys.path.insert(0, ROOT)
     from selective_state_space_ssm_amd import build as _b
     h = hashlib.sha256()
-    with open(os.path.join(pkg, "csrc", "ssm_fwd.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("ssm_fwd.hip", "ssm_device.h"):
+        with open(os.path.join(pkg, "csrc", name), "rb") as f:
+            h.update(f.read())
     h.update(" ".join(_b.FLAGS).encode())
     return h.hexdigest()[:16]
 
