@@ -154,6 +154,59 @@ int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L
                       int *plan, int *states_per_lane, int64_t *chunk);
 
 /*
+ * ssm_scan_bwd -- gradients of ssm_scan_fwd by chunked recomputation
+ * ([Scan page] §4.2: the forward keeps only the state at every chunk
+ * boundary, the backward re-runs each chunk from its boundary state and
+ * walks it back; [Mamba-2 page] §4.3 on recomputing chunk by chunk).
+ * The loss is taken as sum(dy * y) + sum(dlast * last_state), so dy and
+ * dlast are the incoming gradients of the forward's outputs.  With
+ * s_t = C_t . h_t + D u_t (y = s silu(z), or s without a gate) and
+ * g_t = dLoss/dh_t:
+ *     gs_t = dy_t silu(z_t);   g_t = C_t gs_t + a_{t+1} g_{t+1},  g_L = dlast
+ *     du     = D gs + Delta sum_n g B            ddelta = dDelta * sigmoid(x)
+ *     dDelta = u sum_n g B + sum_n g a h_{t-1} A     (without softplus: ddelta = dDelta)
+ *     dz     = dy s silu'(z)                     dA[d,n] = sum_{b,t} g a h_{t-1} Delta
+ *     dB[b,n,t] = sum_d g Delta u                dC[b,n,t] = sum_d gs h
+ *     dD[d]  = sum_{b,t} gs u                    ddelta_bias[d] = sum_{b,t} ddelta
+ *     dh0    = a_0 g_0
+ *   u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0 : the forward's
+ *                  inputs, as for ssm_scan_fwd_states (h0 nullable: zero).
+ *   chunk_states : [batch, K, d_inner, d_state] float32, K = ceil(L /
+ *                  state_chunk), as written by ssm_scan_fwd_states for the
+ *                  same inputs and state_chunk (required).
+ *   state_chunk  : a multiple of 32, at most 512.
+ *   dy           : [batch, d_inner, L], dtype `dtype`, gradient of y.
+ *   dlast        : [batch, d_inner, d_state] float32, gradient of last_state,
+ *                  nullable (zero).
+ *   du, ddelta   : [batch, d_inner, L], dtype `dtype`, outputs.
+ *   dz           : [batch, d_inner, L], dtype `dtype`, output; required if
+ *                  and only if z is given.
+ *   dA           : [d_inner, d_state] float32 output.
+ *   dB, dC       : [batch, d_state, L] float32 outputs (float32 for either
+ *                  dtype: they are sums over d_inner channels).
+ *   dD, ddelta_bias : [d_inner] float32 outputs, nullable (not computed); the
+ *                  gradient is that at the given value, or at zero when D or
+ *                  delta_bias is NULL.
+ *   dh0          : [batch, d_inner, d_state] float32 output, nullable.
+ *   states_per_lane : 2 or 4 (0 = automatic), as for ssm_scan_fwd_plan.
+ * Outputs must not overlap each other or any input.  dA, dB, dC, dD and
+ * ddelta_bias are sums over workgroups taken with float32 atomic adds: their
+ * rounding depends on the order in which workgroups finish, so repeated runs
+ * agree to float32 rounding, not bit for bit.  The library clears them on
+ * `stream` before accumulating.  No memory is allocated.
+ * Errors: SSM_EINVAL (bad pointer, size, flag or state_chunk; overlap;
+ * misaligned pointer), SSM_EUNSUPPORTED (dtype, d_state > 16), SSM_EHIP.
+ */
+int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 const float *h0, const float *chunk_states, int64_t state_chunk,
+                 const void *dy, const float *dlast,
+                 void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz,
+                 float *ddelta_bias, float *dh0,
+                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                 int dtype, int states_per_lane, void *stream);
+
+/*
  * ssm_step -- one recurrent step of the selective scan for every (batch,
  * channel): the constant-time inference form of the recurrence
  * ([Mamba-2 page] §7; the step itself is [Scan page] §1.2):

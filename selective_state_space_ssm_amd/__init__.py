@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_bwd", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,9 @@ def load_library():
     lib.ssm_scan_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_fwd_states.restype = I
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I, P]
+    lib.ssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
+                                 I64, I64, I64, I64, I, I, P]
+    lib.ssm_scan_bwd.restype = I
     lib.ssm_step.restype = I
     lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
                                       ctypes.POINTER(I64)]
@@ -217,6 +220,71 @@ def ssm_scan_fwd_states(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B
                                      SSM_F32 if dt == torch.float32 else SSM_BF16, PLANS[plan], _stream(device))
     _check(rc)
     return y, last_state, chunk_states
+
+
+def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 chunk_states: torch.Tensor, state_chunk: int, dy: torch.Tensor,
+                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                 h0: Optional[torch.Tensor] = None, dlast: Optional[torch.Tensor] = None,
+                 states_per_lane: int = 0, want_dD: bool = True, want_ddelta_bias: bool = True,
+                 want_dh0: bool = True) -> dict:
+    """Gradients of the selective scan (see ``ssm_scan_bwd`` in
+    include/ssm_scan.h) from the chunk states that ``ssm_scan_fwd_states``
+    wrote with the same inputs and ``state_chunk``.
+
+    dy: gradient of y (dtype of u); dlast: gradient of last_state (float32,
+    or None).  Returns a dict with du, ddelta, dz (dtype of u; dz None without
+    z), dA [d, n], dB, dC [b, n, L] (float32), dD, ddelta_bias [d] and dh0
+    [b, d, n] (float32; None where not asked for).
+    """
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_bwd needs CUDA/HIP tensors")
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [b, d, L] and A [d, n]")
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    dt = u.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    for t, name, shape in ((u, "u", (bsz, dim, L)), (delta, "delta", (bsz, dim, L)), (B, "B", (bsz, n, L)),
+                           (C, "C", (bsz, n, L)), (dy, "dy", (bsz, dim, L))):
+        _need(t, name, dt, device, shape)
+    _need(A, "A", torch.float32, device, (dim, n))
+    if state_chunk <= 0:
+        raise ValueError("state_chunk must be positive")
+    _need(chunk_states, "chunk_states", torch.float32, device, (bsz, -(-L // state_chunk), dim, n))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    if D is not None:
+        _need(D, "D", torch.float32, device, (dim,))
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", torch.float32, device, (dim,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, device, (bsz, dim, n))
+    if dlast is not None:
+        _need(dlast, "dlast", torch.float32, device, (bsz, dim, n))
+    f32 = dict(device=device, dtype=torch.float32)
+    out = {
+        "du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+        "dz": torch.empty_like(u) if z is not None else None,
+        "dA": torch.empty((dim, n), **f32), "dB": torch.empty((bsz, n, L), **f32),
+        "dC": torch.empty((bsz, n, L), **f32),
+        "dD": torch.empty((dim,), **f32) if want_dD else None,
+        "ddelta_bias": torch.empty((dim,), **f32) if want_ddelta_bias else None,
+        "dh0": torch.empty((bsz, dim, n), **f32) if want_dh0 else None,
+    }
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                              int(bool(delta_softplus)), _ptr(h0), _ptr(chunk_states), int(state_chunk), _ptr(dy),
+                              _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                              _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                              _ptr(out["dh0"]), bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16,
+                              int(states_per_lane), _stream(device))
+    _check(rc)
+    return out
 
 
 def ssm_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

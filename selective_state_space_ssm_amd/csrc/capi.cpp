@@ -78,6 +78,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    then the fix-up) so that about eight workgroups run per CU.
 int states_for(int64_t wgs) { return wgs >= 6 * kCUs ? 4 : 2; }
 
+// Backward: four states per lane once every SIMD gets two or more
+// wavefronts of one-wavefront workgroups, else two (two wavefronts each).
+int bwd_states_for(int64_t groups) { return groups >= 8 * kCUs ? 4 : 2; }
+
 void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
   (void)dstate;
   const int64_t groups = batch * ceil_div(dim, kGroup);
@@ -291,6 +295,68 @@ int ssm_step(const void* u, const void* delta, const float* A, const void* B, co
   a.batch = batch; a.dim = d_inner; a.dstate = d_state; a.softplus = delta_softplus;
   hipError_t e = ssm::launch_step(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "recurrent step launch");
+  return SSM_OK;
+}
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                 const float* chunk_states, int64_t state_chunk, const void* dy, const float* dlast, void* du,
+                 void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int states_per_lane,
+                 void* stream) {
+  g_err.clear();
+  if (!u || !delta || !A || !B || !C || !chunk_states || !dy || !du || !ddelta || !dA || !dB || !dC)
+    return fail(SSM_EINVAL, "u, delta, A, B, C, chunk_states, dy, du, ddelta, dA, dB and dC must not be NULL");
+  if ((z != nullptr) != (dz != nullptr)) return fail(SSM_EINVAL, "dz must be given if and only if z is");
+  if (int rc = check_sizes(batch, d_inner, d_state, L)) return rc;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
+  if (state_chunk <= 0 || state_chunk % ssm::rows_time_tile() != 0 || state_chunk > ssm::kBwdMaxChunk)
+    return fail(SSM_EINVAL, "state_chunk must be a positive multiple of %d and at most %d (got %lld)",
+                ssm::rows_time_tile(), ssm::kBwdMaxChunk, (long long)state_chunk);
+  if (states_per_lane != 0 && states_per_lane != 2 && states_per_lane != 4)
+    return fail(SSM_EINVAL, "states_per_lane must be 0, 2 or 4 for the backward (got %d)", states_per_lane);
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, chunk_states, dy, dlast,
+                        du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const uint64_t es = dtype == SSM_F32 ? 4 : 2;
+  const uint64_t K = uint64_t(ceil_div(L, state_chunk));
+  const uint64_t nbdl = uint64_t(batch) * d_inner * L, nbnl = uint64_t(batch) * d_state * L;
+  const uint64_t nbdn = uint64_t(batch) * d_inner * d_state, ndn = uint64_t(d_inner) * d_state;
+  const Range rin[] = {range_of(u, nbdl * es), range_of(delta, nbdl * es), range_of(z, nbdl * es),
+                       range_of(dy, nbdl * es), range_of(B, nbnl * es), range_of(C, nbnl * es),
+                       range_of(A, ndn * 4), range_of(D, uint64_t(d_inner) * 4),
+                       range_of(delta_bias, uint64_t(d_inner) * 4), range_of(h0, nbdn * 4),
+                       range_of(chunk_states, K * nbdn * 4), range_of(dlast, nbdn * 4)};
+  const Range rout[] = {range_of(du, nbdl * es), range_of(ddelta, nbdl * es), range_of(dz, nbdl * es),
+                        range_of(dA, ndn * 4), range_of(dB, nbnl * 4), range_of(dC, nbnl * 4),
+                        range_of(dD, uint64_t(d_inner) * 4), range_of(ddelta_bias, uint64_t(d_inner) * 4),
+                        range_of(dh0, nbdn * 4)};
+  for (size_t i = 0; i < sizeof(rout) / sizeof(rout[0]); ++i) {
+    for (const Range& r : rin)
+      if (overlap(rout[i], r)) return fail(SSM_EINVAL, "gradient outputs must not overlap any input");
+    for (size_t j = i + 1; j < sizeof(rout) / sizeof(rout[0]); ++j)
+      if (overlap(rout[i], rout[j])) return fail(SSM_EINVAL, "gradient outputs must not overlap each other");
+  }
+  const int64_t groups = batch * ceil_div(d_inner, kGroup);
+  const int S = states_per_lane != 0 ? states_per_lane : bwd_states_for(groups);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ssm::launch_zero(dA, int64_t(ndn), st);
+  if (e == hipSuccess) e = ssm::launch_zero(dB, int64_t(nbnl), st);
+  if (e == hipSuccess) e = ssm::launch_zero(dC, int64_t(nbnl), st);
+  if (e == hipSuccess && dD) e = ssm::launch_zero(dD, d_inner, st);
+  if (e == hipSuccess && ddelta_bias) e = ssm::launch_zero(ddelta_bias, d_inner, st);
+  if (e != hipSuccess) return hip_fail(e, "gradient clear launch");
+  ssm::BwdArgs a{};
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = h0; a.chunk_states = chunk_states; a.dy = dy; a.dlast = dlast;
+  a.du = du; a.ddelta = ddelta; a.dz = dz; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dbias = ddelta_bias;
+  a.dh0 = dh0;
+  a.batch = batch; a.dim = d_inner; a.dstate = d_state; a.L = L; a.state_chunk = state_chunk;
+  a.softplus = delta_softplus;
+  e = ssm::launch_bwd(a, dtype == SSM_BF16, S, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return SSM_OK;
 }
 

@@ -70,6 +70,41 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
 
+// Gradients of the selective scan by chunked recomputation from the states
+// the forward kept at every state_chunk boundary.
+struct BwdArgs {
+  const void* u;              // [b][d][L]
+  const void* delta;          // [b][d][L]
+  const float* A;             // [d][n]
+  const void* B;              // [b][n][L]
+  const void* C;              // [b][n][L]
+  const float* D;             // [d] nullable
+  const void* z;              // [b][d][L] nullable: no gate
+  const float* bias;          // [d] nullable
+  const float* h0;            // [b][d][n] nullable (zero)
+  const float* chunk_states;  // [b][K][d][n], entry k = state after step min((k+1)*sc, L) - 1
+  const void* dy;             // [b][d][L]
+  const float* dlast;         // [b][d][n] nullable (zero)
+  void* du;                   // [b][d][L]
+  void* ddelta;               // [b][d][L]
+  void* dz;                   // [b][d][L], iff z
+  float* dA;                  // [d][n], accumulated: zeroed by the caller of launch_bwd
+  float* dB;                  // [b][n][L], accumulated
+  float* dC;                  // [b][n][L], accumulated
+  float* dD;                  // [d] nullable, accumulated
+  float* dbias;               // [d] nullable, accumulated
+  float* dh0;                 // [b][d][n] nullable, written
+  int64_t batch, dim, dstate, L;
+  int64_t state_chunk;        // sc: multiple of the backward tile, at most kBwdMaxChunk
+  int softplus;
+};
+constexpr int kBwdTile = 16;       // steps per backward tile
+constexpr int kBwdMaxChunk = 512;  // largest state_chunk (LDS holds one state per tile of a chunk)
+size_t bwd_smem_bytes(int S, int64_t state_chunk);
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int S, hipStream_t st);
+// Fill n floats with zero (a kernel, not a memset).
+hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
+
 // affine_scan association-order constants and launcher
 constexpr int kAffT = 8;      // items per lane
 constexpr int kAffLanes = 64; // lanes per wave

@@ -148,3 +148,44 @@ def test_step_rejects_bad_arguments():
     assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # y on the state
     bad = list(base); bad[8] = 3
     assert lib.ssm_step(*bad, *ok_sizes) == ssm.SSM_EINVAL                      # softplus flag
+
+
+def test_bwd_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    # u, delta, A, B, C, D, z, delta_bias, softplus, h0, chunk_states, state_chunk, dy, dlast,
+    # du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0
+    base = [P(BIG), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, P(6 * BIG), None, 1, None,
+            P(7 * BIG), 64, P(8 * BIG), None, P(9 * BIG), P(10 * BIG), P(11 * BIG), P(12 * BIG), P(13 * BIG),
+            None, P(14 * BIG), None, None]
+    sizes = [2, 64, 16, 256, 0, 0, None]   # batch, d_inner, d_state, L, dtype, states_per_lane, stream
+
+    def call(args=None, sz=None):
+        return lib.ssm_scan_bwd(*(args or base), *(sz or sizes))
+
+    def with_(**kw):
+        idx = {"u": 0, "z": 6, "h0": 9, "cs": 10, "sc": 11, "dy": 12, "du": 14, "dA": 16, "dB": 17, "dC": 18,
+               "dz": 20}
+        a = list(base)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return a
+
+    assert call(with_(cs=None)) == ssm.SSM_EINVAL                   # chunk states are required
+    for sc in (0, 16, 48, 544, 1024, -32):                          # multiple of 32, at most 512
+        assert call(with_(sc=sc)) == ssm.SSM_EINVAL, sc
+    assert call(with_(dz=None)) == ssm.SSM_EINVAL                   # z given without dz
+    assert call(with_(z=None)) == ssm.SSM_EINVAL                    # dz given without z
+    assert call(with_(du=P(BIG))) == ssm.SSM_EINVAL                 # output on an input
+    assert call(with_(dC=P(12 * BIG))) == ssm.SSM_EINVAL            # outputs overlap each other
+    assert call(with_(dA=P(11 * BIG + 4))) == ssm.SSM_EINVAL        # misaligned
+    assert call(with_(dy=None)) == ssm.SSM_EINVAL                   # null dy
+    for spl in (1, 3, 8):
+        s2 = list(sizes); s2[5] = spl
+        assert call(sz=s2) == ssm.SSM_EINVAL, spl
+    s2 = list(sizes); s2[2] = 17
+    assert call(sz=s2) == ssm.SSM_EUNSUPPORTED                      # d_state > 16
+    s2 = list(sizes); s2[4] = 7
+    assert call(sz=s2) == ssm.SSM_EUNSUPPORTED                      # dtype
+    bad = list(base); bad[8] = 2
+    assert call(bad) == ssm.SSM_EINVAL                              # softplus flag

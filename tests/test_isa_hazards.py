@@ -2,10 +2,13 @@
 cannot see: the inline-asm v_mul_f32_dpp / v_fmac_f32_dpp read their DPP
 source (src0) through a cross-lane broadcast, and gfx9 requires two wait
 states between a VALU write of a VGPR and a DPP read of it.  The kernels
-keep those sources load-only; this test compiles ssm_fwd.hip to assembly
-(CPU only) and fails if any VALU instruction writes the source of any DPP
-instruction within the two instructions before it, or if standalone
-broadcasts (v_mov_b32_dpp, one extra instruction per state-step) appear."""
+keep those sources load-only; this test compiles the forward and backward
+kernels to assembly (CPU only) and fails if any VALU instruction writes the
+source of any DPP instruction within the two instructions before it, or if
+standalone broadcasts (v_mov_b32_dpp, one extra instruction per state-step)
+appear.  It also checks that no kernel writes through the scalar data cache
+(scalar stores or atomics, cache write-back or discard): every store of the
+library is a vector store."""
 import os
 import re
 import subprocess
@@ -18,14 +21,27 @@ CSRC = os.path.join(ROOT, "selective_state_space_ssm_amd", "csrc")
 pytestmark = pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def isa(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "ssm_fwd.s"
+SOURCES = ["ssm_fwd.hip", "ssm_bwd.hip", "ssm_step.hip", "affine_scan.hip"]
+
+
+def _compile(tmp_dir, src):
+    out = tmp_dir / (src + ".s")
     cmd = ["/opt/rocm/bin/hipcc", "-O3", "--offload-arch=gfx950", "-std=c++17", "-ffp-contract=off",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, "ssm_fwd.hip"), "-o", str(out)]
+           "-I", CSRC, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def all_isa(tmp_path_factory):
+    d = tmp_path_factory.mktemp("isa")
+    return {src: _compile(d, src) for src in SOURCES}
+
+
+@pytest.fixture(scope="module", params=["ssm_fwd.hip", "ssm_bwd.hip"])
+def isa(request, all_isa):
+    return all_isa[request.param]
 
 
 def _instructions(text):
@@ -86,3 +102,10 @@ def test_row_broadcasts_are_fused(isa):
     fused = sum(1 for op, a in ins if "row_newbcast" in a and op != "v_mov_b32_dpp")
     loose = sum(1 for op, a in ins if "row_newbcast" in a and op == "v_mov_b32_dpp")
     assert fused > 0 and loose == 0, (fused, loose)
+
+
+def test_no_scalar_cache_writes(all_isa):
+    bad = re.compile(r"^(s_store|s_buffer_store|s_scratch_store|s_atomic|s_buffer_atomic|s_dcache_wb|s_dcache_discard)")
+    for src, text in all_isa.items():
+        for op, args in _instructions(text):
+            assert not bad.match(op), f"{src}: scalar-cache write {op} {args}"

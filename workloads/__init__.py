@@ -143,3 +143,17 @@ def random_A(d: int, n: int, device="cpu", seed: int = 1) -> torch.Tensor:
     g = torch.Generator(device=torch.device(device))
     g.manual_seed(seed)
     return -torch.exp(torch.randn((d, n), generator=g, device=device, dtype=torch.float32))
+
+
+def make_grads(w: Workload, device="cpu", seed: int = 0) -> dict:
+    """Incoming gradients for the backward pass of workload ``w``: dy ~ N(0,1)
+    [b, d, L] in the workload's storage type and dlast ~ N(0,1) [b, d, n]
+    float32, drawn in that order with a generator seeded with ``seed + 1000``
+    (so that they do not repeat the input draws)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 1000)
+    f32 = dict(device=dev, dtype=torch.float32)
+    dy = torch.randn((w.batch, w.dim, w.L), generator=g, **f32).to(w.torch_dtype).contiguous()
+    dlast = torch.randn((w.batch, w.dim, w.dstate), generator=g, **f32)
+    return dict(dy=dy, dlast=dlast)
