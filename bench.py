@@ -60,6 +60,11 @@ def parse():
     p.add_argument("--decode", type=int, default=0, metavar="BATCH",
                    help="time ssm_step (one recurrent decode step) for BATCH sequences of the workload's "
                         "layer shape instead of the scan")
+    p.add_argument("--bwd", action="store_true",
+                   help="time the backward pass (ssm_scan_bwd, gradients of every input) instead of the "
+                        "forward; the chunk states come from one untimed ssm_scan_fwd_states call")
+    p.add_argument("--bwd-state-chunk", type=int, default=128,
+                   help="state_chunk of the forward checkpoints the backward recomputes from")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -174,6 +179,130 @@ def decode_bench(args):
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg}), flush=True)
 
 
+# Backward roofline: the arithmetic the chunked recomputation cannot avoid
+# per (channel, state, step): the step again (exp, 2 mul, fma: 5 slots, plus
+# the fma of C.h for the gate's derivative) and the way back (C*gs, the fma
+# of g, g*h_{t-1}*a, fma into dA, fma into the Delta sum, fma of g.B, and the
+# two products summed into dB and dC: 9 slots), 15 issue slots carrying
+# 7 + 13 = 20 FLOP.
+BWD_SLOTS_PER_STATE_STEP = 15.0
+BWD_FLOP_PER_STATE_STEP = 20.0
+BWD_ALU_PEAK_TFLOPS = LANE_SLOTS_PER_S / BWD_SLOTS_PER_STATE_STEP * BWD_FLOP_PER_STATE_STEP / 1e12
+
+
+def bwd_algorithmic_bytes(w, state_chunk: int) -> int:
+    """Every input of the backward read once (u, delta, z, dy, B, C, A, D,
+    bias, the chunk states, dlast) and every gradient written once (du,
+    ddelta, dz, dB, dC in float32, dA, dD, ddelta_bias, dh0)."""
+    s = 4 if w.dtype == "f32" else 2
+    g = 1 if w.gated else 0
+    nbdl = w.batch * w.dim * w.L
+    nbnl = w.batch * w.dstate * w.L
+    nbdn = w.batch * w.dim * w.dstate
+    K = -(-w.L // state_chunk)
+    reads = nbdl * s * (3 + g) + 2 * nbnl * s + 4 * w.dim * w.dstate + 8 * w.dim + 4 * nbdn * (K + 1)
+    writes = nbdl * s * (2 + g) + 2 * nbnl * 4 + 4 * w.dim * w.dstate + 8 * w.dim + 4 * nbdn
+    return reads + writes
+
+
+def bwd_cpu_baseline(inp, gr, w, budget_s):
+    """The float64 C gradient oracle, as it is, on a bounded sample of whole
+    batch rows of the workload (the first channels of row 0 when one row
+    alone exceeds the budget); throughput scaled by state-steps to the
+    workload's GB/s."""
+    import numpy as np
+    from oracle import build as ob, cpu
+    if not os.path.exists(ob.LIB):
+        ob.build()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    host = {k: (None if inp.get(k) is None else inp[k].float().cpu().numpy())
+            for k in ("u", "delta", "z", "A", "B", "C", "D", "delta_bias")}
+    ghost = {k: gr[k].float().cpu().numpy() for k in ("dy", "dlast")}
+
+    def run(nb, nd):
+        sl = lambda x: None if x is None else np.ascontiguousarray(x[:nb, :nd])
+        pv = lambda x: None if x is None else np.ascontiguousarray(x[:nd])
+        t0 = time.perf_counter()
+        cpu.bwd_full(sl(host["u"]), sl(host["delta"]), pv(host["A"]), np.ascontiguousarray(host["B"][:nb]),
+                     np.ascontiguousarray(host["C"][:nb]), D=pv(host["D"]), z=sl(host["z"]),
+                     delta_bias=pv(host["delta_bias"]), delta_softplus=w.softplus, dy=sl(ghost["dy"]),
+                     dlast=sl(ghost["dlast"]), nthreads=threads)
+        return time.perf_counter() - t0
+
+    n0 = min(w.dim, max(threads, 32))
+    t_small = run(1, n0)
+    per_row = t_small * w.dim / n0
+    if per_row > budget_s:
+        nb, nd = 1, int(min(w.dim, max(n0, n0 * budget_s / max(t_small, 1e-6))))
+    else:
+        nb, nd = int(min(w.batch, max(1, budget_s // max(per_row, 1e-6)))), w.dim
+    elapsed = run(nb, nd)
+    frac = nb * nd / (w.batch * w.dim)
+    gbs = bwd_algorithmic_bytes(w, 128) * frac / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb} of {w.batch} batch rows x {nd} of {w.dim} channels x {w.L} steps x {w.dstate} states "
+                      f"({elapsed:.1f} s, float64 C gradient oracle, OpenMP static over channels)",
+            "gsteps_ch_state_per_s": round(w.state_steps() * frac / elapsed / 1e9, 4)}
+
+
+def bwd_bench(args):
+    """Time ssm_scan_bwd (clearing the summed gradients, then the backward
+    kernel) on the workload, from chunk states written by one untimed
+    forward with --bwd-state-chunk."""
+    import torch
+    import selective_state_space_ssm_amd as ssm
+    import workloads
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(w, device=dev, seed=0)
+    gr = workloads.make_grads(w, device=dev, seed=0)
+    sc = args.bwd_state_chunk
+    _, _, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                       inp["delta_bias"], delta_softplus=w.softplus, state_chunk=sc)
+
+    def step():
+        ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, gr["dy"], D=inp["D"],
+                         z=inp["z"], delta_bias=inp["delta_bias"], delta_softplus=w.softplus, dlast=gr["dlast"],
+                         states_per_lane=args.states_per_lane)
+
+    warm = max(3, args.warmup // 10)
+    steps = max(1, args.steps // 4)
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev0.elapsed_time(ev1) / steps
+    bytes_alg = bwd_algorithmic_bytes(w, sc)
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    tflops = w.state_steps() * BWD_FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "selective-scan bwd GB/s (algorithmic bytes of the gradients pass); Gsteps.ch.state/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)",
+        "data": "synthetic (seeded; shapes and value recipes of the workload)",
+        "config": {"workload": w.name + "-bwd", "batch": w.batch, "d_inner": w.dim, "d_state": w.dstate,
+                   "seq_len": w.L, "io_dtype": w.dtype, "gated": w.gated, "state_chunk": sc,
+                   "states_per_lane": args.states_per_lane},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(BWD_ALU_PEAK_TFLOPS, 2),
+                     "unit": "TFLOP/s", "frac": round(tflops / BWD_ALU_PEAK_TFLOPS, 4), "traffic": None},
+        "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": bytes_alg},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = bwd_cpu_baseline(inp, gr, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(inp, w, budget_s):
     """The float64 C oracle, as it is, on a bounded sample of whole channels
     of the same workload; throughput scaled to the workload's GB/s."""
@@ -222,6 +351,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
     import torch
 

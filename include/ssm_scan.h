@@ -188,7 +188,7 @@ int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L
  *                  gradient is that at the given value, or at zero when D or
  *                  delta_bias is NULL.
  *   dh0          : [batch, d_inner, d_state] float32 output, nullable.
- *   states_per_lane : 2 or 4 (0 = automatic), as for ssm_scan_fwd_plan.
+ *   states_per_lane : 1, 2 or 4 (0 = automatic), as for ssm_scan_fwd_plan.
  * Outputs must not overlap each other or any input.  dA, dB, dC, dD and
  * ddelta_bias are sums over workgroups taken with float32 atomic adds: their
  * rounding depends on the order in which workgroups finish, so repeated runs

@@ -78,9 +78,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    then the fix-up) so that about eight workgroups run per CU.
 int states_for(int64_t wgs) { return wgs >= 6 * kCUs ? 4 : 2; }
 
-// Backward: four states per lane once every SIMD gets two or more
-// wavefronts of one-wavefront workgroups, else two (two wavefronts each).
-int bwd_states_for(int64_t groups) { return groups >= 8 * kCUs ? 4 : 2; }
+// Backward states per lane, measured on MI355X: four once every SIMD gets
+// two or more one-wavefront workgroups (the 1.4B shape: 2048 groups); one
+// (four wavefronts per group) when there are fewer groups than SIMDs (the
+// 130m shape: 768 groups, three wavefronts per SIMD), where latency hiding
+// outweighs the extra cross-row sums; two in between.
+int bwd_states_for(int64_t groups) { return groups >= 8 * kCUs ? 4 : (groups >= 4 * kCUs ? 2 : 1); }
 
 void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
   (void)dstate;
@@ -314,8 +317,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   if (state_chunk <= 0 || state_chunk % ssm::rows_time_tile() != 0 || state_chunk > ssm::kBwdMaxChunk)
     return fail(SSM_EINVAL, "state_chunk must be a positive multiple of %d and at most %d (got %lld)",
                 ssm::rows_time_tile(), ssm::kBwdMaxChunk, (long long)state_chunk);
-  if (states_per_lane != 0 && states_per_lane != 2 && states_per_lane != 4)
-    return fail(SSM_EINVAL, "states_per_lane must be 0, 2 or 4 for the backward (got %d)", states_per_lane);
+  if (states_per_lane != 0 && states_per_lane != 1 && states_per_lane != 2 && states_per_lane != 4)
+    return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", states_per_lane);
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, chunk_states, dy, dlast,
                         du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0};
   for (const void* q : ptrs)

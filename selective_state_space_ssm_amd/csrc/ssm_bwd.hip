@@ -176,9 +176,9 @@ struct BwdSz {
 
 }  // namespace
 
-// S: states per lane (2 or 4); workgroup = 16 channels x 16 states in 4/S
-// wavefronts; grid (ceil(d_inner/16), batch).  With S = 2 the tile's a_t are
-// kept in registers; with S = 4 they are recomputed on the way back (the
+// S: states per lane (1, 2 or 4); workgroup = 16 channels x 16 states in
+// 4/S wavefronts; grid (ceil(d_inner/16), batch).  With S <= 2 the tile's a_t
+// are kept in registers; with S = 4 they are recomputed on the way back (the
 // registers for them are not there).
 template <typename IO, int S, bool GATED, bool VEC>
 __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz p) {
@@ -188,11 +188,12 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   constexpr int NT = 64 * W;
   constexpr int V = kCG * kBT / NT;             // prep / epilogue steps per thread
   constexpr int TPC = kBT / V;                  // prep / epilogue threads per channel
-  constexpr int BCQ = 2 * kNS * kBT / 4 / NT;   // B/C float4 groups per thread
-  constexpr bool kKeepA = S == 2;
+  constexpr int BCG = 2 * kNS * kBT / 4;        // B/C float4 groups per tile
+  constexpr int BCQ = (BCG + NT - 1) / NT;       // per thread (the first BCG threads with S = 1)
+  constexpr bool kKeepA = S <= 2;
   constexpr uint32_t ES = sizeof(T);
-  static_assert(S == 2 || S == 4, "S");
-  static_assert(V * NT == kCG * kBT && BCQ * NT * 4 == 2 * kNS * kBT, "tiling");
+  static_assert(S == 1 || S == 2 || S == 4, "S");
+  static_assert(V * NT == kCG * kBT && BCG % 64 == 0, "tiling");
 
   extern __shared__ float smem[];
   float* sDt = smem;                    // [16][kBR] Delta2
@@ -256,14 +257,17 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   const Rsrc rC = make_rsrc(a.Cg + b * N * L, bc_bytes);
   const uint32_t poff = static_cast<uint32_t>((pc * L + pt) * ES);
 
-  // B/C groups of this thread: group q = tid + i*NT covers 4 steps of state
-  // (q/4) % 16 of B (q < 64) or C; its LDS slot is sBC + 4q.
+  // B/C groups of this thread: group q = tid + i*NT (q < BCG; whole waves
+  // have a group or none) covers 4 steps of state (q/4) % 16 of B (q < 64)
+  // or C; its LDS slot is sBC + 4q.
   uint32_t bcoff[BCQ];
-  bool bcis_c[BCQ];
+  bool bcis_c[BCQ], bchas[BCQ];
 #pragma unroll
   for (int i = 0; i < BCQ; ++i) {
     const int q = tid + i * NT;
-    bcis_c[i] = __builtin_amdgcn_readfirstlane(wave * 64 + i * NT) >= kNS * kBT / 4;
+    const int q0 = __builtin_amdgcn_readfirstlane(wave * 64 + i * NT);
+    bchas[i] = q0 < BCG;
+    bcis_c[i] = q0 >= kNS * kBT / 4;
     const int n = (q / (kBT / 4)) % kNS;
     bcoff[i] = static_cast<uint32_t>((n * L + (q % (kBT / 4)) * 4) * ES);
   }
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
       }
 #pragma unroll
       for (int i = 0; i < BCQ; ++i)
-        if (FULL || !bcis_c[i]) Buf::template ldw<4>(bcis_c[i] ? rC : rB, bcoff[i] + toff, R.wbc[i]);
+        if (bchas[i] && (FULL || !bcis_c[i])) Buf::template ldw<4>(bcis_c[i] ? rC : rB, bcoff[i] + toff, R.wbc[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
       }
 #pragma unroll
       for (int i = 0; i < BCQ; ++i)
-        if (FULL || !bcis_c[i])
+        if (bchas[i] && (FULL || !bcis_c[i]))
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             Buf::template ldw<1>(bcis_c[i] ? rC : rB, bcoff[i] + toff + e * ES, &R.wbc[i][e]);
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     F32::template st<V>(sDu + pc * kBR + pt, du);
 #pragma unroll
     for (int i = 0; i < BCQ; ++i)
-      if (!bcis_c[i]) *reinterpret_cast<float4*>(sBC + (tid + i * NT) * 4) = unpack_bc(R, i);
+      if (bchas[i] && !bcis_c[i]) *reinterpret_cast<float4*>(sBC + (tid + i * NT) * 4) = unpack_bc(R, i);
   };
 
   // ---- phase-2 prep; e* keep what the epilogue of the same tile needs
@@ -385,6 +389,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     F32::template st<V>(sGs + pc * kBR + pt, gsv);
 #pragma unroll
     for (int i = 0; i < BCQ; ++i) {
+      if (!bchas[i]) continue;
       const int q = tid + i * NT;
       float4 v = unpack_bc(R, i);
       if (!full) {
@@ -597,6 +602,16 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   TileRegs R;
   using kPart = std::integral_constant<bool, false>;
   using kFullLoad = std::integral_constant<bool, true>;
+  // The first tile of the last chunk is loaded here; the first tile of every
+  // earlier chunk (always a whole chunk, so phase 1 runs) during the last tile
+  // of the chunk after it, and phase 2's first tile during phase 1's last.
+  {
+    const int cs = (K - 1) * sc;
+    if (Li - cs > kBT)
+      load_tile(R, cs, kPart{});
+    else
+      load_tile(R, cs, kFullLoad{});
+  }
 #pragma unroll 1
   for (int k = K - 1; k >= 0; --k) {
     const int cs = k * sc;
@@ -619,11 +634,13 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
       myCk[s * kCG] = v;
     }
     // phase 1: states at the start of tiles 1 .. nt-1 (all full tiles)
-    if (nt > 1) load_tile(R, cs, kPart{});
 #pragma unroll 1
     for (int i = 0; i + 1 < nt; ++i) {
       prep1(R);
-      if (i + 2 < nt) load_tile(R, cs + (i + 1) * kBT, kPart{});
+      if (i + 2 < nt)
+        load_tile(R, cs + (i + 1) * kBT, kPart{});
+      else
+        load_tile(R, cs + (nt - 1) * kBT, kFullLoad{});
       __syncthreads();
       recur1(h);
 #pragma unroll
@@ -631,12 +648,14 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
       __syncthreads();
     }
     // phase 2: tiles from last to first
-    load_tile(R, cs + (nt - 1) * kBT, kFullLoad{});
 #pragma unroll 1
     for (int i = nt - 1; i >= 0; --i) {
       const int t0 = cs + i * kBT;
       prep2(R, t0, ce);
-      if (i > 0) load_tile(R, t0 - kBT, kFullLoad{});
+      if (i > 0)
+        load_tile(R, t0 - kBT, kFullLoad{});
+      else if (k > 0)
+        load_tile(R, cs - sc, kPart{});
       __syncthreads();
       float hst[S];
 #pragma unroll
@@ -708,8 +727,12 @@ static hipError_t launch_bwd_s(const BwdArgs& h, hipStream_t st) {
 }
 
 hipError_t launch_bwd(const BwdArgs& h, bool bf16, int S, hipStream_t st) {
-  if (bf16) return S == 4 ? launch_bwd_s<BF16, 4>(h, st) : launch_bwd_s<BF16, 2>(h, st);
-  return S == 4 ? launch_bwd_s<F32, 4>(h, st) : launch_bwd_s<F32, 2>(h, st);
+  if (bf16) {
+    if (S == 4) return launch_bwd_s<BF16, 4>(h, st);
+    return S == 2 ? launch_bwd_s<BF16, 2>(h, st) : launch_bwd_s<BF16, 1>(h, st);
+  }
+  if (S == 4) return launch_bwd_s<F32, 4>(h, st);
+  return S == 2 ? launch_bwd_s<F32, 2>(h, st) : launch_bwd_s<F32, 1>(h, st);
 }
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st) {

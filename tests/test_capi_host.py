@@ -180,7 +180,7 @@ def test_bwd_rejects_bad_arguments():
     assert call(with_(dC=P(12 * BIG))) == ssm.SSM_EINVAL            # outputs overlap each other
     assert call(with_(dA=P(11 * BIG + 4))) == ssm.SSM_EINVAL        # misaligned
     assert call(with_(dy=None)) == ssm.SSM_EINVAL                   # null dy
-    for spl in (1, 3, 8):
+    for spl in (3, 8, -1):
         s2 = list(sizes); s2[5] = spl
         assert call(sz=s2) == ssm.SSM_EINVAL, spl
     s2 = list(sizes); s2[2] = 17

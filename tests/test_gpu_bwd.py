@@ -90,8 +90,10 @@ def check(got, want, dtype, label):
 
 CASES = [
     # b, d, n, L, state_chunk, S
+    (1, 16, 16, 64, 32, 1),
     (1, 16, 16, 64, 32, 2),
     (1, 16, 16, 64, 32, 4),
+    (2, 40, 16, 150, 64, 1),
     (2, 40, 16, 150, 64, 2),
     (2, 40, 16, 150, 64, 4),
     (1, 32, 16, 517, 128, 0),
@@ -115,7 +117,7 @@ def test_bwd_matches_oracle(case, dtype):
     dict(gated=False, softplus=True, with_D=True, with_bias=True, with_h0=False, with_dlast=True),
     dict(gated=True, softplus=False, with_D=False, with_bias=True, with_h0=True, with_dlast=False),
 ], ids=["bare", "nogate", "nosoftplus"])
-@pytest.mark.parametrize("S", [2, 4])
+@pytest.mark.parametrize("S", [1, 2, 4])
 def test_bwd_optional_inputs(flags, S):
     inp = make(2, 33, 16, 200, torch.float32, seed=5, **flags)
     if not flags["softplus"]:
