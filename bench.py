@@ -65,6 +65,11 @@ def parse():
                         "forward; the chunk states come from one untimed ssm_scan_fwd_states call")
     p.add_argument("--bwd-state-chunk", type=int, default=128,
                    help="state_chunk of the forward checkpoints the backward recomputes from")
+    p.add_argument("--conv", type=int, default=0, metavar="K",
+                   help="time ssm_scan_fwd_conv: the scan with a K-tap causal conv1d + SiLU fused in front "
+                        "(the workload's u is taken as the conv input x)")
+    p.add_argument("--conv-u-out", action="store_true",
+                   help="with --conv, also write u = silu(conv1d(x))")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -372,7 +377,28 @@ def main():
 
     use_states = args.h0 or args.state_chunk > 0
     extra_bytes = 0
-    if use_states:
+    if args.conv:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        conv_w = torch.randn((w.dim, args.conv), generator=g, device=dev) * (1.0 / args.conv)
+        conv_b = torch.randn((w.dim,), generator=g, device=dev) * 0.1
+        u_out = torch.empty_like(inp["u"]) if args.conv_u_out else None
+        extra_bytes = 4 * w.dim * (args.conv + 1) + (w.batch * w.dim * w.L * (4 if w.dtype == "f32" else 2)
+                                                     if args.conv_u_out else 0)
+        lib = ssm.load_library()
+        es = ssm.SSM_F32 if w.dtype == "f32" else ssm.SSM_BF16
+        P = ssm._ptr
+        plan_id = ssm.PLANS[args.plan]
+        stream_ptr = ssm._stream(dev)
+
+        def step():
+            rc = lib.ssm_scan_fwd_conv(P(inp["u"]), P(conv_w), P(conv_b), args.conv, P(inp["delta"]), P(inp["A"]),
+                                       P(inp["B"]), P(inp["C"]), P(inp["D"]), P(inp["z"]), P(inp["delta_bias"]),
+                                       int(w.softplus), None, P(y), P(last), P(u_out), None, 0, w.batch, w.dim,
+                                       w.dstate, w.L, es, plan_id, stream_ptr)
+            if rc != 0:
+                raise RuntimeError(lib.ssm_last_error().decode())
+    elif use_states:
         g = torch.Generator(device=dev)
         g.manual_seed(1)
         h0 = torch.randn((w.batch, w.dim, w.dstate), generator=g, device=dev) if args.h0 else None
@@ -417,7 +443,7 @@ def main():
     if args.plan != "auto":
         plan["plan"] = args.plan
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
-    traffic = None if use_states else measured_traffic(w.name, plan)
+    traffic = None if (use_states or args.conv) else measured_traffic(w.name, plan)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -435,6 +461,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "d_inner": w.dim, "d_state": w.dstate, "seq_len": w.L,
                    "io_dtype": w.dtype, "gated": w.gated, "plan": plan,
                    **({"h0": True} if args.h0 else {}),
+                   **({"conv_k": args.conv, "u_out": bool(args.conv_u_out)} if args.conv else {}),
                    **({"state_chunk": args.state_chunk} if args.state_chunk else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),

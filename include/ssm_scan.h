@@ -154,6 +154,31 @@ int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L
                       int *plan, int *states_per_lane, int64_t *chunk);
 
 /*
+ * ssm_scan_fwd_conv -- ssm_scan_fwd_states with the causal depthwise conv1d
+ * and SiLU of the Mamba block fused in front of the scan ([Mamba-2 page]
+ * §4.1: Conv1D, the SSM scan and SiLU in one kernel so the intermediate
+ * never goes to HBM).  The scan's input u is computed in the kernel:
+ *     u[b,d,t] = silu(conv_b[d] + sum_{k<K} conv_w[d,k] * x[b,d,t-(K-1)+k]),
+ * x at steps before 0 being zero (a causal convolution with K-1 steps of
+ * left padding; conv_w[d, K-1] multiplies the current step).
+ *   x      : [batch, d_inner, L], dtype `dtype`, the conv's input.
+ *   conv_w : [d_inner, conv_k] float32; conv_k = 1 .. 4.
+ *   conv_b : [d_inner] float32, nullable (zero).
+ *   u_out  : [batch, d_inner, L], dtype `dtype`, output of u, nullable (u is
+ *            then never written; it is recomputed from x wherever needed).
+ * Other arguments, semantics and errors as ssm_scan_fwd_states (with
+ * SSM_EUNSUPPORTED for conv_k outside 1..4).  u enters the scan at float32:
+ * with SSM_BF16 it is not rounded to bfloat16 first (u_out is).
+ */
+int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_k,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                      const float *h0, void *y, float *last_state, void *u_out,
+                      float *chunk_states, int64_t state_chunk,
+                      int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                      int dtype, int plan, void *stream);
+
+/*
  * ssm_scan_bwd -- gradients of ssm_scan_fwd by chunked recomputation
  * ([Scan page] §4.2: the forward keeps only the state at every chunk
  * boundary, the backward re-runs each chunk from its boundary state and

@@ -54,6 +54,7 @@ __all__ = [
     "selective_scan_fwd",
     "selective_scan_bruteforce",
     "selective_scan_bwd",
+    "causal_conv1d",
     "affine_scan",
     "lti_closed_form",
 ]
@@ -447,6 +448,35 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     dx = ddt * (1.0 / (1.0 + np.exp(-x))) if delta_softplus else ddt
     return {"du": du, "ddelta": dx, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dz": dz,
             "ddelta_bias": dx.sum(axis=(0, 2)), "dh0": dh0}
+
+
+def causal_conv1d(x, w, b=None, activation: Optional[str] = "silu"):
+    """Depthwise causal 1-D convolution of every channel, float64, then the
+    activation (SiLU by default, None for none): the Conv1D in front of the
+    SSM in the Mamba block ([Mamba-2 page] §4.1 names Conv1D and SiLU among
+    the fused operators).  The pages give no formula; the reading taken is
+    the usual causal one with K-1 steps of zero left padding:
+
+        out[b,d,t] = b[d] + sum_{k=0}^{K-1} w[d,k] * x[b,d,t-(K-1)+k],
+
+    x at steps below 0 being zero, so w[d, K-1] multiplies the current step.
+    x: [b, d, L]; w: [d, K]; b: [d] or None.
+    """
+    x = _f64(x)
+    w = _f64(w)
+    bsz, dim, L = x.shape
+    K = w.shape[1]
+    out = np.zeros((bsz, dim, L)) if b is None else np.broadcast_to(_f64(b)[None, :, None], (bsz, dim, L)).copy()
+    for k in range(K):
+        shift = K - 1 - k              # w[:, k] multiplies x[t - shift]
+        if shift >= L:
+            continue
+        out[:, :, shift:] += w[None, :, k, None] * x[:, :, :L - shift]
+    if activation == "silu":
+        out = silu(out)
+    elif activation is not None:
+        raise ValueError("activation must be 'silu' or None")
+    return out
 
 
 def lti_closed_form(a: float, b):

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_bwd", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,9 @@ def load_library():
     lib.ssm_scan_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_fwd_states.restype = I
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I, P]
+    lib.ssm_scan_fwd_conv.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                      I, I, P]
+    lib.ssm_scan_fwd_conv.restype = I
     lib.ssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
                                  I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_bwd.restype = I
@@ -220,6 +223,58 @@ def ssm_scan_fwd_states(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B
                                      SSM_F32 if dt == torch.float32 else SSM_BF16, PLANS[plan], _stream(device))
     _check(rc)
     return y, last_state, chunk_states
+
+
+def ssm_scan_fwd_conv(x: torch.Tensor, conv_w: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                      B: torch.Tensor, C: torch.Tensor, conv_b: Optional[torch.Tensor] = None,
+                      D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                      delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                      h0: Optional[torch.Tensor] = None, state_chunk: int = 0, plan: str = "auto",
+                      return_u: bool = False):
+    """Selective scan with the causal depthwise conv1d + SiLU in front (see
+    ``ssm_scan_fwd_conv`` in include/ssm_scan.h): u = silu(conv1d(x)) is
+    computed in the kernel.  conv_w: [d, K] float32 (K = 1..4), conv_b: [d].
+
+    Returns (y, last_state, chunk_states or None, u or None).
+    """
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_fwd_conv needs CUDA/HIP tensors")
+    if x.dim() != 3 or A.dim() != 2 or conv_w.dim() != 2:
+        raise ValueError("x must be [b, d, L], A [d, n] and conv_w [d, K]")
+    bsz, dim, L = x.shape
+    n = A.shape[1]
+    K = conv_w.shape[1]
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    for t, name, shape in ((x, "x", (bsz, dim, L)), (delta, "delta", (bsz, dim, L)), (B, "B", (bsz, n, L)),
+                           (C, "C", (bsz, n, L))):
+        _need(t, name, dt, device, shape)
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(conv_w, "conv_w", torch.float32, device, (dim, K))
+    for t, name in ((conv_b, "conv_b"), (D, "D"), (delta_bias, "delta_bias")):
+        if t is not None:
+            _need(t, name, torch.float32, device, (dim,))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, device, (bsz, dim, n))
+    if plan not in PLANS:
+        raise ValueError(f"plan must be one of {list(PLANS)}")
+    y = torch.empty_like(x)
+    last = torch.empty((bsz, dim, n), device=device, dtype=torch.float32)
+    cs = (torch.empty((bsz, -(-L // state_chunk), dim, n), device=device, dtype=torch.float32)
+          if state_chunk > 0 else None)
+    u = torch.empty_like(x) if return_u else None
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_fwd_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), int(K), _ptr(delta), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                   _ptr(y), _ptr(last), _ptr(u), _ptr(cs), int(state_chunk), bsz, dim, n, L,
+                                   SSM_F32 if dt == torch.float32 else SSM_BF16, PLANS[plan], _stream(device))
+    _check(rc)
+    return y, last, cs, u
 
 
 def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -131,7 +131,8 @@ int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t L) {
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int delta_softplus, const float* h0, void* y,
                   float* last_state, float* chunk_states, int64_t state_chunk, int64_t batch, int64_t dim,
-                  int64_t dstate, int64_t L, int dtype, int plan, int S_req, int64_t chunk_req, void* stream) {
+                  int64_t dstate, int64_t L, int dtype, int plan, int S_req, int64_t chunk_req, const float* conv_w, const float* conv_b,
+                  int conv_k, void* u_out, void* stream) {
   g_err.clear();
   if (!u || !delta || !A || !B || !C || !y)
     return fail(SSM_EINVAL, "u, delta, A, B, C and y must not be NULL");
@@ -146,7 +147,11 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (chunk_states != nullptr && (state_chunk <= 0 || state_chunk % ssm::rows_time_tile() != 0))
     return fail(SSM_EINVAL, "state_chunk must be a positive multiple of %d when chunk_states is given",
                 ssm::rows_time_tile());
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, chunk_states};
+  if (conv_w == nullptr && (conv_b != nullptr || u_out != nullptr))
+    return fail(SSM_EINVAL, "conv_b and u_out need conv_w");
+  if (conv_w != nullptr && (conv_k < 1 || conv_k > 4))
+    return fail(SSM_EUNSUPPORTED, "conv_k must be 1 to 4 (got %d)", conv_k);
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, chunk_states, conv_w, conv_b, u_out};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
 
@@ -157,13 +162,17 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   const Range rin[] = {range_of(u, nbdl * es), range_of(delta, nbdl * es), range_of(z, nbdl * es),
                        range_of(B, nbnl * es), range_of(C, nbnl * es), range_of(A, uint64_t(dim) * dstate * 4),
                        range_of(D, uint64_t(dim) * 4), range_of(delta_bias, uint64_t(dim) * 4),
-                       range_of(h0, nstate * 4)};
+                       range_of(h0, nstate * 4), range_of(conv_w, uint64_t(dim) * (conv_w ? conv_k : 0) * 4),
+                       range_of(conv_b, uint64_t(dim) * 4)};
   const Range ry = range_of(y, nbdl * es);
   const Range rl = range_of(last_state, nstate * 4);
   const Range rc = range_of(chunk_states, nsc * nstate * 4);
+  const Range ru = range_of(u_out, nbdl * es);
   for (const Range& r : rin)
-    if (overlap(ry, r) || overlap(rl, r) || overlap(rc, r)) return fail(SSM_EINVAL, "outputs must not overlap inputs");
-  if (overlap(ry, rl) || overlap(ry, rc) || overlap(rl, rc)) return fail(SSM_EINVAL, "outputs overlap each other");
+    if (overlap(ry, r) || overlap(rl, r) || overlap(rc, r) || overlap(ru, r))
+      return fail(SSM_EINVAL, "outputs must not overlap inputs");
+  if (overlap(ry, rl) || overlap(ry, rc) || overlap(rl, rc) || overlap(ru, ry) || overlap(ru, rl) || overlap(ru, rc))
+    return fail(SSM_EINVAL, "outputs overlap each other");
 
   int pl, S;
   int64_t chunk;
@@ -184,6 +193,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   a.y = y; a.last_state = last_state; a.h_init = nullptr; a.agg_p = nullptr; a.agg_h = nullptr;
   a.h0 = h0; a.chunk_states = chunk_states; a.state_chunk = chunk_states ? state_chunk : 0;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.L = L; a.softplus = delta_softplus;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = conv_w ? conv_k : 0; a.u_out = u_out;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SSM_BF16;
 
@@ -238,7 +248,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const void* z, const float* delta_bias, int delta_softplus, void* y, float* last_state,
                  int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
-                       d_inner, d_state, L, dtype, SSM_PLAN_AUTO, 0, 0, stream);
+                       d_inner, d_state, L, dtype, SSM_PLAN_AUTO, 0, 0, nullptr, nullptr, 0, nullptr, stream);
 }
 
 int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -246,7 +256,7 @@ int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const vo
                       float* last_state, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
                       int plan, int states_per_lane, int64_t chunk, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
-                       d_inner, d_state, L, dtype, plan, states_per_lane, chunk, stream);
+                       d_inner, d_state, L, dtype, plan, states_per_lane, chunk, nullptr, nullptr, 0, nullptr, stream);
 }
 
 int ssm_scan_fwd_states(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -254,7 +264,20 @@ int ssm_scan_fwd_states(const void* u, const void* delta, const float* A, const 
                         void* y, float* last_state, float* chunk_states, int64_t state_chunk, int64_t batch,
                         int64_t d_inner, int64_t d_state, int64_t L, int dtype, int plan, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, y, last_state, chunk_states,
-                       state_chunk, batch, d_inner, d_state, L, dtype, plan, 0, 0, stream);
+                       state_chunk, batch, d_inner, d_state, L, dtype, plan, 0, 0, nullptr, nullptr, 0, nullptr,
+                       stream);
+}
+
+int ssm_scan_fwd_conv(const void* x, const float* conv_w, const float* conv_b, int conv_k, const void* delta,
+                      const float* A, const void* B, const void* C, const float* D, const void* z,
+                      const float* delta_bias, int delta_softplus, const float* h0, void* y, float* last_state,
+                      void* u_out, float* chunk_states, int64_t state_chunk, int64_t batch, int64_t d_inner,
+                      int64_t d_state, int64_t L, int dtype, int plan, void* stream) {
+  g_err.clear();
+  if (!conv_w) return fail(SSM_EINVAL, "conv_w must not be NULL");
+  return scan_fwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, y, last_state, chunk_states,
+                       state_chunk, batch, d_inner, d_state, L, dtype, plan, 0, 0, conv_w, conv_b, conv_k, u_out,
+                       stream);
 }
 
 int ssm_scan_plan_for(int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int* plan,

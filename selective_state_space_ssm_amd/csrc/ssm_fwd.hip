@@ -81,7 +81,8 @@ constexpr int kRow = kTT + 4;    // LDS row stride in floats (float4 rows, stagg
 // block (block-local thread `tid`, wave `wave`), over channels [c0, c0+16)
 // of batch row b and chunk k, with its LDS at `smem`.  Template: storage
 // IO, states per lane S (1, 2, 4), mode, GATED (z present), VEC (L is a
-// multiple of 8: vector loads and stores).  Every wave of the block calls
+// multiple of 8: vector loads and stores), CONV (u = silu(causal conv1d of
+// x) computed in prep from x and the conv weights, [Mamba-2 page] §4.1).  Every wave of the block calls
 // __syncthreads() in the same sequence (all groups of a block have the same
 // tile count).  Pointers: the caller guarantees that outputs overlap no
 // input.
@@ -103,9 +104,12 @@ struct RowArgs {
   float* chunk_states;
   float* agg_p;
   float* agg_h;
+  const float* convw;      // CONV: [d][K] causal conv1d weights (u then points at x)
+  const float* convb;      // CONV: [d] conv bias, nullable
+  typename IO::T* uo;      // CONV: [b][d][L] silu(conv1d(x)) output, nullable
 };
 
-template <typename IO, int S, int MODE, bool GATED, bool VEC>
+template <typename IO, int S, int MODE, bool GATED, bool VEC, bool CONV>
 __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSizes& p, float* smem, int tid,
                                            int wave, int64_t c0, int64_t b, int64_t k) {
   using T = typename IO::T;
@@ -220,8 +224,10 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   // words per tile row slice and per B/C group: packed (VEC) or one per element
   constexpr int RW = VEC ? Buf::template kWords<V> : V;
   constexpr int BW = VEC ? Buf::template kWords<4> : 4;
+  constexpr int HW = CONV ? 3 : 0;  // conv halo: the 3 steps before the slot
   struct TileRegs {
     uint32_t wu[RW], wd[RW], wz[RW];
+    uint32_t wh[HW > 0 ? HW : 1];
     uint32_t wbc[BCQ][BW];
     int t0;  // first step of the tile the words hold
   };
@@ -237,6 +243,12 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       for (int e = 0; e < RW; ++e) wz[e] = 0u;
     }
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if constexpr (CONV) {
+      // x at steps pt-3 .. pt-1 of the tile (before step 0 of channel 0 the
+      // offset wraps past the resource and reads zero; prep zeroes the rest)
+#pragma unroll
+      for (int j = 0; j < HW; ++j) Buf::template ldw<1>(rU, poff + toff - (HW - j) * ES, &R.wh[j]);
+    }
     if constexpr (VEC) {
       Buf::template ldw<V>(rU, poff + toff, wu);
       Buf::template ldw<V>(rD, poff + toff, wd);
@@ -269,6 +281,8 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     auto& wbc = R.wbc;
 #pragma unroll
     for (int e = 0; e < RW; ++e) asm volatile("" : "+v"(wu[e]), "+v"(wd[e]), "+v"(wz[e]));
+#pragma unroll
+    for (int j = 0; j < HW; ++j) asm volatile("" : "+v"(R.wh[j]));
 #pragma unroll
     for (int i = 0; i < BCQ; ++i)
 #pragma unroll
@@ -318,9 +332,52 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 #pragma unroll
     for (int e = 0; e < V; ++e) asm volatile("" : "+v"(nDu[e]), "+v"(nG[e]));
   };
+
+  // ---- causal conv1d + SiLU in front of the scan (CONV): with K taps
+  // right-aligned in w4 (w4[3] multiplies x_t, w4[3-j] multiplies x_{t-j}),
+  // u_t = silu(bias + sum_j w4[j] x_{t-3+j}), x before step 0 being zero.
+  // u replaces the loaded x in ru; with an output it is also stored.
+  float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cbias = 0.0f;
+  if constexpr (CONV) {
+    const int K = p.convk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (pvalid && j >= 4 - K) w4[j] = args.convw[pd * K + (j - (4 - K))];
+    cbias = (pvalid && args.convb != nullptr) ? args.convb[pd] : 0.0f;
+  }
+  const Rsrc rUO = make_rsrc(CONV && MODE == kFull && args.uo != nullptr ? args.uo + row0 : u + row0,
+                             CONV && MODE == kFull && args.uo != nullptr ? in_bytes : 0u);
+  auto conv_front = [&](TileRegs& R, int r_t0) {
+    float xs[V + 3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      float v;
+      Buf::template unpack<1>(&R.wh[j], &v);
+      xs[j] = (r_t0 + pt - 3 + j >= 0) ? v : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) xs[3 + e] = ru[e];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float pre = cbias;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pre = __builtin_fmaf(w4[j], xs[e + j], pre);
+      ru[e] = silu(pre);
+    }
+    const uint32_t toff = static_cast<uint32_t>(r_t0) * ES;
+    if (VEC && r_t0 + kTT <= t_end) {
+      Buf::template st<V>(rUO, poff + toff, ru);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (r_t0 + pt + e < t_end) Buf::template st<1>(rUO, poff + toff + e * ES, &ru[e]);
+    }
+  };
   auto prep = [&](TileRegs& R) {
     unpack_tile(R);
     const int r_t0 = R.t0;
+    if constexpr (CONV) conv_front(R, r_t0);
     float dt[V], du[V];
     if (r_t0 + kTT <= t_end) {
 #pragma unroll
@@ -543,14 +600,14 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 //    groups [0, 2*pairs) belong to two-group blocks and the rest to
 //    one-group blocks.
 // --------------------------------------------------------------------------
-template <typename IO, int S, int MODE, bool GATED, bool VEC>
+template <typename IO, int S, int MODE, bool GATED, bool VEC, bool CONV>
 __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(RowArgs<IO> args, CsSizes p) {
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
   // the wave index as an SGPR keeps every per-wave quantity uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  rows_group<IO, S, MODE, GATED, VEC>(args, p, smem, tid, wave, static_cast<int64_t>(blockIdx.x) * kCG,
-                                      blockIdx.y, blockIdx.z);
+  rows_group<IO, S, MODE, GATED, VEC, CONV>(args, p, smem, tid, wave, static_cast<int64_t>(blockIdx.x) * kCG,
+                                            blockIdx.y, blockIdx.z);
 }
 
 struct MixedSizes {
@@ -558,7 +615,7 @@ struct MixedSizes {
   int64_t singles;  // one-group blocks per batch row
 };
 
-template <typename IO, int MODE, bool GATED, bool VEC>
+template <typename IO, int MODE, bool GATED, bool VEC, bool CONV>
 __global__ __launch_bounds__(256, 2) void ssm_mixed_kernel(RowArgs<IO> args, CsSizes p, MixedSizes m,
                                                            int smem_pair_floats) {
   extern __shared__ float smem[];
@@ -570,13 +627,13 @@ __global__ __launch_bounds__(256, 2) void ssm_mixed_kernel(RowArgs<IO> args, CsS
     const int sub = wave >> 1;
     const int64_t b = x / m.pairs;
     const int64_t g = 2 * (x % m.pairs) + sub;
-    rows_group<IO, 2, MODE, GATED, VEC>(args, p, smem + sub * smem_pair_floats, tid - 128 * sub, wave & 1,
-                                        g * kCG, b, blockIdx.z);
+    rows_group<IO, 2, MODE, GATED, VEC, CONV>(args, p, smem + sub * smem_pair_floats, tid - 128 * sub, wave & 1,
+                                              g * kCG, b, blockIdx.z);
   } else {
     const int64_t q = x - nA;
     const int64_t b = q / m.singles;
     const int64_t g = 2 * m.pairs + q % m.singles;
-    rows_group<IO, 1, MODE, GATED, VEC>(args, p, smem, tid, wave, g * kCG, b, blockIdx.z);
+    rows_group<IO, 1, MODE, GATED, VEC, CONV>(args, p, smem, tid, wave, g * kCG, b, blockIdx.z);
   }
 }
 
@@ -625,6 +682,7 @@ static RowArgs<IO> row_args(const FwdArgs& a) {
   r.zg = static_cast<const T*>(a.z); r.biasg = a.bias; r.yg = static_cast<T*>(a.y);
   r.last_state = a.last_state; r.h_init = a.h_init; r.h0 = a.h0; r.chunk_states = a.chunk_states;
   r.agg_p = a.agg_p; r.agg_h = a.agg_h;
+  r.convw = a.conv_w; r.convb = a.conv_b; r.uo = static_cast<T*>(a.u_out);
   return r;
 }
 
@@ -632,15 +690,16 @@ static CsSizes cs_sizes(const FwdArgs& a) {
   CsSizes sz;
   sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.chunk = a.chunk; sz.softplus = a.softplus;
   sz.state_chunk = a.chunk_states != nullptr ? a.state_chunk : 0;
+  sz.convk = a.conv_w != nullptr ? a.conv_k : 0;
   return sz;
 }
 
-template <typename IO, int S, int MODE, bool GATED, bool VEC>
+template <typename IO, int S, int MODE, bool GATED, bool VEC, bool CONV>
 static hipError_t launch_rows_v(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((a.dim + kCG - 1) / kCG), static_cast<unsigned>(a.batch),
                   static_cast<unsigned>(nchunks));
   const size_t smem = rows_smem_bytes(S, MODE);
-  auto kern = ssm_rows_kernel<IO, S, MODE, GATED, VEC>;
+  auto kern = ssm_rows_kernel<IO, S, MODE, GATED, VEC, CONV>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
@@ -648,7 +707,7 @@ static hipError_t launch_rows_v(const FwdArgs& a, int64_t nchunks, hipStream_t s
   return hipGetLastError();
 }
 
-template <typename IO, int MODE, bool GATED, bool VEC>
+template <typename IO, int MODE, bool GATED, bool VEC, bool CONV>
 static hipError_t launch_mixed_v(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
   const int64_t groups = (a.dim + kCG - 1) / kCG;
   MixedSizes m;
@@ -657,7 +716,7 @@ static hipError_t launch_mixed_v(const FwdArgs& a, int64_t pairs, int64_t nchunk
   const size_t pair_bytes = rows_smem_bytes(2, MODE);
   const size_t smem = (2 * pair_bytes > rows_smem_bytes(1, MODE)) ? 2 * pair_bytes : rows_smem_bytes(1, MODE);
   const dim3 grid(static_cast<unsigned>(a.batch * (m.pairs + m.singles)), 1, static_cast<unsigned>(nchunks));
-  auto kern = ssm_mixed_kernel<IO, MODE, GATED, VEC>;
+  auto kern = ssm_mixed_kernel<IO, MODE, GATED, VEC, CONV>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
@@ -666,28 +725,40 @@ static hipError_t launch_mixed_v(const FwdArgs& a, int64_t pairs, int64_t nchunk
   return hipGetLastError();
 }
 
-template <typename IO, int MODE>
-static hipError_t dispatch_mixed(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
+template <typename IO, int MODE, bool CONV>
+static hipError_t dispatch_mixed_c(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
   const bool vec = a.L % 8 == 0;
   if constexpr (MODE == kFull) {
     if (a.z != nullptr)
-      return vec ? launch_mixed_v<IO, MODE, true, true>(a, pairs, nchunks, st)
-                 : launch_mixed_v<IO, MODE, true, false>(a, pairs, nchunks, st);
+      return vec ? launch_mixed_v<IO, MODE, true, true, CONV>(a, pairs, nchunks, st)
+                 : launch_mixed_v<IO, MODE, true, false, CONV>(a, pairs, nchunks, st);
   }
-  return vec ? launch_mixed_v<IO, MODE, false, true>(a, pairs, nchunks, st)
-             : launch_mixed_v<IO, MODE, false, false>(a, pairs, nchunks, st);
+  return vec ? launch_mixed_v<IO, MODE, false, true, CONV>(a, pairs, nchunks, st)
+             : launch_mixed_v<IO, MODE, false, false, CONV>(a, pairs, nchunks, st);
+}
+
+template <typename IO, int MODE>
+static hipError_t dispatch_mixed(const FwdArgs& a, int64_t pairs, int64_t nchunks, hipStream_t st) {
+  return a.conv_w != nullptr ? dispatch_mixed_c<IO, MODE, true>(a, pairs, nchunks, st)
+                             : dispatch_mixed_c<IO, MODE, false>(a, pairs, nchunks, st);
+}
+
+template <typename IO, int S, int MODE, bool CONV>
+static hipError_t dispatch_flags_c(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
+  const bool vec = a.L % 8 == 0;
+  if constexpr (MODE == kFull) {
+    if (a.z != nullptr)
+      return vec ? launch_rows_v<IO, S, MODE, true, true, CONV>(a, nchunks, st)
+                 : launch_rows_v<IO, S, MODE, true, false, CONV>(a, nchunks, st);
+  }
+  return vec ? launch_rows_v<IO, S, MODE, false, true, CONV>(a, nchunks, st)
+             : launch_rows_v<IO, S, MODE, false, false, CONV>(a, nchunks, st);
 }
 
 template <typename IO, int S, int MODE>
 static hipError_t dispatch_flags(const FwdArgs& a, int64_t nchunks, hipStream_t st) {
-  const bool vec = a.L % 8 == 0;
-  if constexpr (MODE == kFull) {
-    if (a.z != nullptr)
-      return vec ? launch_rows_v<IO, S, MODE, true, true>(a, nchunks, st)
-                 : launch_rows_v<IO, S, MODE, true, false>(a, nchunks, st);
-  }
-  return vec ? launch_rows_v<IO, S, MODE, false, true>(a, nchunks, st)
-             : launch_rows_v<IO, S, MODE, false, false>(a, nchunks, st);
+  return a.conv_w != nullptr ? dispatch_flags_c<IO, S, MODE, true>(a, nchunks, st)
+                             : dispatch_flags_c<IO, S, MODE, false>(a, nchunks, st);
 }
 
 template <typename IO, int MODE>

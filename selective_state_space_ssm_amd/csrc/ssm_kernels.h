@@ -29,6 +29,10 @@ struct FwdArgs {
   int64_t batch, dim, dstate, L;
   int64_t chunk;            // steps per chunk (grid z); = L for one chunk
   int softplus;
+  const float* conv_w;      // nullable: [d][conv_k] causal conv1d in front (u then holds x)
+  const float* conv_b;      // [d] nullable
+  int conv_k;               // 1..4 taps
+  void* u_out;              // nullable: [b][d][L] silu(conv1d(x)), kFull only
 };
 
 // Sizes and flags of one row-layout launch (by value).
@@ -37,6 +41,7 @@ struct CsSizes {
   int64_t chunk;
   int64_t state_chunk;   // chunk_states spacing (0: none)
   int softplus;
+  int convk;             // conv1d taps (0: no conv)
 };
 
 // S = states per lane (1, 2 or 4); a workgroup is 16 channels x 16 states

@@ -389,3 +389,44 @@ def test_start_state_split_invariance():
                                     h0=h1, **kw)
     assert np.max(np.abs(np.concatenate([y1, y2], axis=-1) - y)) <= 1e-13 * np.max(np.abs(y))
     assert np.max(np.abs(h2 - last)) <= 1e-13 * np.max(np.abs(last))
+
+
+# ---------------------------------------------------------------- causal conv1d
+
+def test_causal_conv1d_matches_numpy_convolve():
+    """Each channel's causal convolution is the first L terms of the full
+    discrete convolution np.convolve(x, w[::-1]): with w[K-1] on the current
+    step, the tap on x[t - j] is w[K-1-j], i.e. the reversed taps."""
+    rng = np.random.default_rng(11)
+    for K in (1, 2, 3, 4):
+        x = rng.normal(size=(2, 3, 37))
+        w = rng.normal(size=(3, K))
+        b = rng.normal(size=3)
+        got = ref.causal_conv1d(x, w, b, activation=None)
+        for bi in range(2):
+            for d in range(3):
+                want = np.convolve(x[bi, d], w[d, ::-1])[:37] + b[d]
+                np.testing.assert_allclose(got[bi, d], want, rtol=1e-13, atol=1e-13)
+
+
+def test_causal_conv1d_matches_torch_grouped_conv():
+    """torch.nn.functional.conv1d with groups = channels and K-1 steps of
+    left padding (cross-correlation, w[K-1] on the current step) then SiLU."""
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(2, 5, 50))
+    w = rng.normal(size=(5, 4))
+    b = rng.normal(size=5)
+    got = ref.causal_conv1d(x, w, b)
+    xt = torch.tensor(x)
+    pre = torch.nn.functional.conv1d(torch.nn.functional.pad(xt, (3, 0)), torch.tensor(w)[:, None, :],
+                                     torch.tensor(b), groups=5)
+    want = torch.nn.functional.silu(pre).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_causal_conv1d_single_tap_is_pointwise():
+    rng = np.random.default_rng(13)
+    x = rng.normal(size=(1, 4, 9))
+    w = rng.normal(size=(4, 1))
+    got = ref.causal_conv1d(x, w, None, activation=None)
+    np.testing.assert_allclose(got, x * w[None, :, :], rtol=0, atol=0)
