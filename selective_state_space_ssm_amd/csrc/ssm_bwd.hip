@@ -41,10 +41,10 @@
 //            swaps and three adds) and left in LDS per (wave, channel, step).
 //            dB and dC, sums over the row's 16 channels, go through a DPP
 //            reduce-scatter (after four butterfly stages lane j of a row holds
-//            the sum for one step of its state) fed in bit-reversed step
-//            order so that each stage's pair is ready as soon as its second
-//            half is, and leave the workgroup as one atomic add per
-//            (state, step).
+//            the sum for one step of its state; the first two stages use
+//            bank-masked DPP adds), fed step by step so that each stage's
+//            pair is ready as soon as its second half is, and leave the
+//            workgroup as one atomic add per (state, step).
 //     epilogue + prep (every thread, V steps of one channel): du, ddelta,
 //            dz of this tile from the LDS sums; then Delta2, Delta*u, gs, B
 //            and C of the tile before into LDS, whose global loads were issued
@@ -72,59 +72,84 @@ constexpr int kCG = 16;         // channels per workgroup
 constexpr int kNS = 16;         // state slots per workgroup
 constexpr int kBR = kBT + 4;    // LDS row stride in floats (float4 rows, staggered banks)
 
-// DPP lane patterns within a row of 16 lanes
-constexpr int kRowMirror = 0x140;      // lane l <- 15 - l  (l ^ 15)
-constexpr int kRowHalfMirror = 0x141;  // lane l <- l ^ 7
-constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]: l ^ 2
-constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]: l ^ 1
-
-constexpr int bitrev4(int p) { return ((p & 1) << 3) | ((p & 2) << 1) | ((p & 4) >> 1) | ((p & 8) >> 3); }
+// DPP lane patterns within a row of 16 lanes (lane l reads the lane named)
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: l ^ 1
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: l ^ 2
+constexpr int kRowRor4 = 0x124;   // row_ror:4: (l - 4) mod 16
+constexpr int kRowRor8 = 0x128;   // row_ror:8: (l - 8) mod 16 = l ^ 8
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-// One butterfly stage: of the pair (lo, hi) of values whose index differs in
-// this stage's bit, lanes whose selector bit is set keep hi and send lo to
-// their partner, the others keep lo and send hi.
+// Butterfly stages of the reduce-scatter.  Of a pair (lo, hi) of values
+// whose index differs in this stage's bit, lanes whose selector bit is set
+// end with hi summed with their partner's hi, the others with lo summed with
+// their partner's lo.  Stages 1 and 2 select on lane bits 2 and 3, i.e. on
+// the DPP bank (four consecutive lanes): all lanes add lo, then a
+// bank-masked add overwrites the selected banks with hi (two instructions;
+// s_nop 1 gives the two wait states a DPP read needs after a VALU write of
+// its source).  Stages 3 and 4 select on bits 0 and 1 with v_cndmask (three
+// instructions).
+__device__ __forceinline__ float rs_stage1(float lo, float hi) {
+  float out = lo + dpp_f<kRowRor4>(lo);
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xa"
+      : "+v"(out)
+      : "v"(hi));
+  return out;
+}
+__device__ __forceinline__ float rs_stage2(float lo, float hi) {
+  float out = lo + dpp_f<kRowRor8>(lo);
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "+v"(out)
+      : "v"(hi));
+  return out;
+}
 template <int CTRL>
-__device__ __forceinline__ float rs_stage(float lo, float hi, bool sel_hi) {
+__device__ __forceinline__ float rs_stage_sel(float lo, float hi, bool sel_hi) {
   const float keep = sel_hi ? hi : lo;
   const float send = sel_hi ? lo : hi;
   return keep + dpp_f<CTRL>(send);
 }
 
 // Reduce-scatter of 16 values over the 16 lanes of a row, fed one value at a
-// time.  Value number P (P = 0..15 in the order produced) takes index
-// bitrev4(P); stage k combines indices that differ in bit 3 - k, with the
-// partner lane l ^ 15, l ^ 7, l ^ 2, l ^ 1 and the selector bit 3, 2, 1, 0 of
-// the lane.  Partners agree on every earlier selector bit, so after the four
-// stages lane l holds the sum over all 16 lanes of index l, i.e. of value
-// number bitrev4(l).  Bit reversal makes both halves of every pair
-// consecutive in production order, so at most one value waits per stage.
+// time: value number P (P = 0..15 in the order produced) has index P, and
+// stage k (k = 1..4) combines indices that differ in bit k-1, selecting on
+// lane bit 2, 3, 0, 1 with the partner lane (l - 4) mod 16, l ^ 8, l ^ 1,
+// l ^ 2.  Each partner agrees with the lane on every earlier selector bit
+// and differs in this one; after stage 2 a lane's values are summed over
+// the four lanes that share its bits 0 and 1, after stage 4 over all 16, so
+// lane l holds the full sum of value number
+// rs_value(l) = bit2(l) + 2 bit3(l) + 4 bit0(l) + 8 bit1(l).
+// Both halves of every pair are consecutive in production order, so at most
+// one value waits per stage.
+__device__ __forceinline__ int rs_value(int l) {
+  return ((l >> 2) & 1) | (((l >> 3) & 1) << 1) | ((l & 1) << 2) | (((l >> 1) & 1) << 3);
+}
+
 struct RsTree {
   float p0, p1, p2, p3, out;
 };
 
 template <int P>
-__device__ __forceinline__ void rs_push(RsTree& t, float x, const bool (&sel)[4]) {
+__device__ __forceinline__ void rs_push(RsTree& t, float x, const bool (&sel)[2]) {
   if constexpr ((P & 1) == 0) {
     t.p0 = x;
   } else {
-    const float y1 = rs_stage<kRowMirror>(t.p0, x, sel[0]);
+    const float y1 = rs_stage1(t.p0, x);
     if constexpr (((P >> 1) & 1) == 0) {
       t.p1 = y1;
     } else {
-      const float y2 = rs_stage<kRowHalfMirror>(t.p1, y1, sel[1]);
+      const float y2 = rs_stage2(t.p1, y1);
       if constexpr (((P >> 2) & 1) == 0) {
         t.p2 = y2;
       } else {
-        const float y3 = rs_stage<kQuadSwap2>(t.p2, y2, sel[2]);
+        const float y3 = rs_stage_sel<kQuadSwap1>(t.p2, y2, sel[0]);
         if constexpr (((P >> 3) & 1) == 0)
           t.p3 = y3;
         else
-          t.out = rs_stage<kQuadSwap1>(t.p3, y3, sel[3]);
+          t.out = rs_stage_sel<kQuadSwap2>(t.p3, y3, sel[1]);
       }
     }
   }
@@ -435,7 +460,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   };
 
   // ---- phase 2 compute of one tile
-  const bool sel[4] = {(col & 8) != 0, (col & 4) != 0, (col & 2) != 0, (col & 1) != 0};
+  const bool sel[2] = {(col & 1) != 0, (col & 2) != 0};
   auto compute = [&](const float (&hst)[S], int t0, int t_end, bool last_tile_of_seq) {
     float bc[S], cc[S];
 #pragma unroll
@@ -526,8 +551,9 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
         xw[(q * kCG + col) * kBR + step] = v;
       }
     });
-    // dB, dC of this tile: lane col holds step 15 - bitrev4(col) of its state
-    const int tl = t0 + kBT - 1 - bitrev4(col);
+    // dB, dC of this tile: lane col holds value number rs_value(col), the
+    // value produced at step 15 - rs_value(col)
+    const int tl = t0 + kBT - 1 - rs_value(col);
     if (tl < t_end) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
