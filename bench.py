@@ -348,8 +348,9 @@ def cpu_baseline(inp, w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU scaling is not implemented "
-                                   "(see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this library runs on one GPU only; multi-GPU scaling is not implemented "
+                                   "(the path would shard over independent (batch, channel) rows)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args)
