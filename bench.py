@@ -153,10 +153,21 @@ def decode_bench(args):
     u, dl, z, B, C = (pick(inp[k]) for k in ("u", "delta", "z", "B", "C"))
     state = torch.randn((w.batch, w.dim, w.dstate), device=dev)
     y = torch.empty_like(u)
+    K = args.conv
+    if K:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        conv_w = torch.randn((w.dim, K), generator=g, device=dev) * (1.0 / K)
+        conv_b = torch.randn((w.dim,), generator=g, device=dev) * 0.1
+        conv_state = torch.randn((w.batch, w.dim, K - 1), generator=g, device=dev) if K > 1 else None
 
-    def step():
-        ssm.ssm_step(u, dl, inp["A"], B, C, state, D=inp["D"], z=z, delta_bias=inp["delta_bias"],
-                     delta_softplus=w.softplus, y=y)
+        def step():
+            ssm.ssm_step_conv(u, conv_w, conv_state, dl, inp["A"], B, C, state, conv_b=conv_b, D=inp["D"], z=z,
+                              delta_bias=inp["delta_bias"], delta_softplus=w.softplus, y=y)
+    else:
+        def step():
+            ssm.ssm_step(u, dl, inp["A"], B, C, state, D=inp["D"], z=z, delta_bias=inp["delta_bias"],
+                         delta_softplus=w.softplus, y=y)
 
     for _ in range(args.warmup):
         step()
@@ -174,13 +185,15 @@ def decode_bench(args):
     nbd = w.batch * w.dim
     bytes_alg = (8 * nbd * w.dstate + nbd * es * (3 + int(w.gated)) + 2 * w.batch * w.dstate * es
                  + 4 * w.dim * w.dstate + 8 * w.dim)
+    if K:  # conv state read and written, conv weights and bias
+        bytes_alg += 8 * nbd * (K - 1) + 4 * w.dim * (K + 1)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     print(json.dumps({"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
                       "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
                       "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)", "data": "synthetic",
                       "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
-                                 "d_state": w.dstate, "io_dtype": w.dtype},
+                                 "d_state": w.dstate, "io_dtype": w.dtype, **({"conv_k": K} if K else {})},
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg}), flush=True)
 
 

@@ -255,6 +255,32 @@ int ssm_step(const void *u, const void *delta, const float *A, const void *B, co
              int64_t batch, int64_t d_inner, int64_t d_state, int dtype, void *stream);
 
 /*
+ * ssm_step_conv -- ssm_step with the causal conv1d + SiLU in front, the
+ * decode-time form of ssm_scan_fwd_conv: the conv keeps the K-1 previous
+ * inputs of every channel as its state.  For every (batch, channel):
+ *     window = (conv_state[b,d,0 .. K-2], x[b,d])          oldest first
+ *     u      = silu(conv_b[d] + sum_k conv_w[d,k] * window[k])
+ *     conv_state <- (window[1 .. K-1])                     x enters, the oldest leaves
+ * then the step of ssm_step with u.  T calls over x_1 .. x_T from a zero conv
+ * state and a zero SSM state reproduce ssm_scan_fwd_conv over those T steps.
+ *   x            : [batch, d_inner], dtype `dtype`.
+ *   conv_w       : [d_inner, conv_k] float32, conv_k = 1 .. 4; conv_b: [d_inner]
+ *                  float32, nullable.
+ *   conv_state_in, conv_state_out : [batch, d_inner, conv_k-1] float32 (unused
+ *                  and may be NULL when conv_k = 1); out may equal in (updated
+ *                  in place) or be disjoint from it.
+ *   u_out        : [batch, d_inner], dtype `dtype`, nullable: u of this step.
+ * Other arguments and errors as ssm_step (SSM_EUNSUPPORTED for conv_k outside
+ * 1..4).
+ */
+int ssm_step_conv(const void *x, const float *conv_w, const float *conv_b, int conv_k,
+                  const float *conv_state_in, float *conv_state_out,
+                  const void *delta, const float *A, const void *B, const void *C,
+                  const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                  const float *state_in, float *state_out, void *y, void *u_out,
+                  int64_t batch, int64_t d_inner, int64_t d_state, int dtype, void *stream);
+
+/*
  * affine_scan -- inclusive scan of affine pairs along each row
  * ([Scan page] §1.2 and §2.1; [Mamba-2 page] §2.2).
  * A pair (a, b) is the map h -> a*h + b; composition, later step first, is

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_step", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_step", "ssm_step_conv", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +63,8 @@ def load_library():
     lib.ssm_scan_fwd_conv.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, P, P, P, P, P, I64, I64, I64, I64, I64,
                                       I, I, P]
     lib.ssm_scan_fwd_conv.restype = I
+    lib.ssm_step_conv.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I, P]
+    lib.ssm_step_conv.restype = I
     lib.ssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
                                  I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_bwd.restype = I
@@ -389,6 +391,58 @@ def ssm_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
                           SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
     _check(rc)
     return y, state_out
+
+
+def ssm_step_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_state: Optional[torch.Tensor], delta: torch.Tensor,
+                  A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, state: torch.Tensor,
+                  conv_b: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                  delta_softplus: bool = False, conv_state_out: Optional[torch.Tensor] = None,
+                  state_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                  return_u: bool = False):
+    """One decode step with the causal conv1d + SiLU in front (see
+    ``ssm_step_conv`` in include/ssm_scan.h).  conv_state: [b, d, K-1]
+    float32 (None when K = 1), updated in place unless conv_state_out is
+    given; state likewise.  Returns (y, conv_state_out, state_out, u or None).
+    """
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("ssm_step_conv needs CUDA/HIP tensors")
+    bsz, dim = x.shape
+    n = A.shape[1]
+    K = conv_w.shape[1]
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    for t, name, shape in ((x, "x", (bsz, dim)), (delta, "delta", (bsz, dim)), (B, "B", (bsz, n)),
+                           (C, "C", (bsz, n))):
+        _need(t, name, dt, device, shape)
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(conv_w, "conv_w", torch.float32, device, (dim, K))
+    _need(state, "state", torch.float32, device, (bsz, dim, n))
+    if K > 1:
+        _need(conv_state, "conv_state", torch.float32, device, (bsz, dim, K - 1))
+    for t, name in ((conv_b, "conv_b"), (D, "D"), (delta_bias, "delta_bias")):
+        if t is not None:
+            _need(t, name, torch.float32, device, (dim,))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim))
+    if conv_state_out is None:
+        conv_state_out = conv_state
+    if state_out is None:
+        state_out = state
+    if y is None:
+        y = torch.empty_like(x)
+    u = torch.empty_like(x) if return_u else None
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_step_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), int(K), _ptr(conv_state if K > 1 else None),
+                               _ptr(conv_state_out if K > 1 else None), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(state),
+                               _ptr(state_out), _ptr(y), _ptr(u), bsz, dim, n,
+                               SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
+    _check(rc)
+    return y, conv_state_out, state_out, u
 
 
 def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,

@@ -386,6 +386,59 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   return SSM_OK;
 }
 
+int ssm_step_conv(const void* x, const float* conv_w, const float* conv_b, int conv_k, const float* conv_state_in,
+                  float* conv_state_out, const void* delta, const float* A, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int delta_softplus, const float* state_in,
+                  float* state_out, void* y, void* u_out, int64_t batch, int64_t d_inner, int64_t d_state, int dtype,
+                  void* stream) {
+  g_err.clear();
+  if (!x || !conv_w || !delta || !A || !B || !C || !state_in || !state_out || !y)
+    return fail(SSM_EINVAL, "x, conv_w, delta, A, B, C, state_in, state_out and y must not be NULL");
+  if (int rc = check_sizes(batch, d_inner, d_state, 1)) return rc;
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
+  if (conv_k < 1 || conv_k > 4) return fail(SSM_EUNSUPPORTED, "conv_k must be 1 to 4 (got %d)", conv_k);
+  if (conv_k > 1 && (!conv_state_in || !conv_state_out))
+    return fail(SSM_EINVAL, "conv_state_in and conv_state_out must not be NULL when conv_k > 1");
+  const void* ptrs[] = {x, conv_w, conv_b, conv_state_in, conv_state_out, delta, A, B, C, D, z, delta_bias,
+                        state_in, state_out, y, u_out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const uint64_t es = dtype == SSM_F32 ? 4 : 2;
+  const uint64_t nbd = uint64_t(batch) * d_inner, nbn = uint64_t(batch) * d_state;
+  const uint64_t nstate = nbd * d_state, ncs = nbd * uint64_t(conv_k - 1);
+  const Range rin[] = {range_of(x, nbd * es), range_of(delta, nbd * es), range_of(z, nbd * es),
+                       range_of(B, nbn * es), range_of(C, nbn * es), range_of(A, uint64_t(d_inner) * d_state * 4),
+                       range_of(D, uint64_t(d_inner) * 4), range_of(delta_bias, uint64_t(d_inner) * 4),
+                       range_of(conv_w, uint64_t(d_inner) * conv_k * 4), range_of(conv_b, uint64_t(d_inner) * 4)};
+  const Range ry = range_of(y, nbd * es), ru = range_of(u_out, nbd * es);
+  const Range rsi = range_of(state_in, nstate * 4), rso = range_of(state_out, nstate * 4);
+  const Range rci = range_of(conv_state_in, ncs * 4), rco = range_of(conv_state_out, ncs * 4);
+  for (const Range& r : rin)
+    if (overlap(ry, r) || overlap(ru, r) || overlap(rso, r) || overlap(rsi, r) || overlap(rco, r) || overlap(rci, r))
+      return fail(SSM_EINVAL, "outputs and states must not overlap the other inputs");
+  const Range outs[] = {ry, ru, rso, rco};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SSM_EINVAL, "outputs overlap each other");
+  if (overlap(ry, rsi) || overlap(ry, rci) || overlap(ru, rsi) || overlap(ru, rci) || overlap(rso, rci) ||
+      overlap(rco, rsi))
+    return fail(SSM_EINVAL, "outputs overlap a state input");
+  if (state_in != state_out && overlap(rsi, rso))
+    return fail(SSM_EINVAL, "state_out must equal state_in or be disjoint from it");
+  if (conv_state_in != conv_state_out && overlap(rci, rco))
+    return fail(SSM_EINVAL, "conv_state_out must equal conv_state_in or be disjoint from it");
+  ssm::StepArgs a{};
+  a.u = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.state_in = state_in; a.state_out = state_out; a.y = y;
+  a.batch = batch; a.dim = d_inner; a.dstate = d_state; a.softplus = delta_softplus;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = conv_k; a.conv_state_in = conv_state_in;
+  a.conv_state_out = conv_state_out; a.u_out = u_out;
+  hipError_t e = ssm::launch_step(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "recurrent step launch");
+  return SSM_OK;
+}
+
 int affine_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t rows, int64_t L,
                 void* stream) {
   g_err.clear();

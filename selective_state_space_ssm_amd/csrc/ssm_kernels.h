@@ -72,6 +72,12 @@ struct StepArgs {
   void* y;              // [b][d]
   int64_t batch, dim, dstate;
   int softplus;
+  const float* conv_w;          // nullable: [d][conv_k] conv1d in front (u then holds x_t)
+  const float* conv_b;          // [d] nullable
+  int conv_k;                   // 1..4
+  const float* conv_state_in;   // [b][d][conv_k-1]
+  float* conv_state_out;        // [b][d][conv_k-1], may equal conv_state_in
+  void* u_out;                  // [b][d] nullable
 };
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st);
 

@@ -45,6 +45,19 @@ struct BF16S {
 constexpr int kQuadSwap1 = 0xB1;  // [1, 0, 3, 2]
 constexpr int kQuadSwap2 = 0x4E;  // [2, 3, 0, 1]
 
+// every lane of a quad takes lane J's value
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), J | (J << 2) | (J << 4) | (J << 6), 0xf,
+                                                    0xf, false));
+}
+
+// lane q of a quad takes lane q+1's value (lane 3 its own)
+__device__ __forceinline__ float quad_shift_down(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 1 | (2 << 2) | (3 << 4) | (3 << 6), 0xf,
+                                                    0xf, false));
+}
+
 __device__ __forceinline__ float quad_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xf, 0xf, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xf, 0xf, false));
@@ -55,24 +68,73 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 // Grid: one thread per (channel, quad), 256 threads (64 channels) per block.
 // VEC4: d_state is a multiple of 4 (float4 state and B/C accesses).
-template <typename IO, bool VEC4>
-__global__ __launch_bounds__(256) void ssm_step_kernel(
-    const typename IO::T* __restrict__ u, const typename IO::T* __restrict__ dlt, const float* __restrict__ A,
-    const typename IO::T* __restrict__ B, const typename IO::T* __restrict__ C, const float* __restrict__ D,
-    const typename IO::T* __restrict__ z, const float* __restrict__ bias, const float* state_in,
-    float* state_out, typename IO::T* __restrict__ y, int64_t batch, int64_t dim, int64_t N, int softplus) {
+// CONV: u comes from the causal conv1d + SiLU over the window (conv state,
+// x_t): the conv state [b][d][K-1] holds the K-1 previous inputs, oldest
+// first; u = silu(conv_b + sum_k conv_w[k] window[k]) and the window shifted
+// by one (x_t in, the oldest out) is written back.  The four lanes of a
+// channel all read the state before lane 0 writes it (the stored values
+// depend on the loaded ones), so the update may be in place.
+template <typename IO>
+struct StepDev {
+  const typename IO::T* u;  // x with CONV
+  const typename IO::T* dlt;
+  const float* A;
+  const typename IO::T* B;
+  const typename IO::T* C;
+  const float* D;
+  const typename IO::T* z;
+  const float* bias;
+  const float* state_in;
+  float* state_out;
+  typename IO::T* y;
+  const float* conv_w;
+  const float* conv_b;
+  const float* cs_in;
+  float* cs_out;
+  typename IO::T* u_out;
+  int64_t batch, dim, N;
+  int softplus, conv_k;
+};
+
+template <typename IO, bool VEC4, bool CONV>
+__global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t dim = a.dim, N = a.N;
   const int64_t ch = gid >> 2;  // (b, d) flattened, d fastest
   const int q = static_cast<int>(gid & 3);
-  const bool valid = ch < batch * dim;
+  const bool valid = ch < a.batch * dim;
   const int64_t chc = valid ? ch : 0;
   const int64_t b = chc / dim;
   const int64_t d = chc - b * dim;
 
-  const float uu = IO::ld(u + chc);
-  const float x = IO::ld(dlt + chc) + (bias != nullptr ? bias[d] : 0.0f);
+  float uu;
+  if constexpr (CONV) {
+    const int K = a.conv_k;
+    // lane q of the quad holds conv state element q (q < K-1): the channel's
+    // K-1 floats are read and written by neighbouring lanes, coalesced over
+    // the wave; the four lanes see the whole window through DPP broadcasts.
+    const float xt = IO::ld(a.u + chc);
+    const bool own = valid && q < K - 1;
+    const float sq = own ? a.cs_in[chc * (K - 1) + q] : 0.0f;
+    const float s0 = quad_bcast<0>(sq), s1 = quad_bcast<1>(sq), s2 = quad_bcast<2>(sq);
+    // window oldest first: state[0 .. K-2], then x_t
+    float pre = a.conv_b != nullptr ? a.conv_b[d] : 0.0f;
+    const float* w = a.conv_w + d * K;
+    if (K >= 2) pre = __builtin_fmaf(w[0], s0, pre);
+    if (K >= 3) pre = __builtin_fmaf(w[1], s1, pre);
+    if (K >= 4) pre = __builtin_fmaf(w[2], s2, pre);
+    pre = __builtin_fmaf(w[K - 1], xt, pre);
+    uu = pre * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * pre));
+    // the window moves by one: element q takes element q+1, the last x_t
+    const float next = quad_shift_down(sq);
+    if (own) a.cs_out[chc * (K - 1) + q] = (q < K - 2) ? next : xt;
+    if (valid && q == 0 && a.u_out != nullptr) IO::st(a.u_out + chc, uu);
+  } else {
+    uu = IO::ld(a.u + chc);
+  }
+  const float x = IO::ld(a.dlt + chc) + (a.bias != nullptr ? a.bias[d] : 0.0f);
   float dt = x;
-  if (softplus) {
+  if (a.softplus) {
     // softplus(x) = log(1 + e^x), computed as ln2 * log2(1 + 2^(x log2 e));
     // x itself above 44 (where e^-x is below float32 resolution)
     const float sp = 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e));
@@ -83,6 +145,11 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(
 
   float part = 0.0f;
   const int64_t n0 = 4 * q;
+  const float* state_in = a.state_in;
+  float* state_out = a.state_out;
+  const float* A = a.A;
+  const typename IO::T* B = a.B;
+  const typename IO::T* C = a.C;
   if (valid && n0 < N) {
     const int64_t so = ch * N + n0;
     float h[4], bv[4], cv[4], av[4];
@@ -121,29 +188,34 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(
   }
   const float tot = quad_sum(part);
   if (valid && q == 0) {
-    float yv = tot + (D != nullptr ? D[d] : 0.0f) * uu;
-    if (z != nullptr) {
-      const float zz = IO::ld(z + chc);
+    float yv = tot + (a.D != nullptr ? a.D[d] : 0.0f) * uu;
+    if (a.z != nullptr) {
+      const float zz = IO::ld(a.z + chc);
       yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * zz));
     }
-    IO::st(y + chc, yv);
+    IO::st(a.y + chc, yv);
   }
 }
 
 template <typename IO>
-static hipError_t launch_step_t(const StepArgs& a, hipStream_t st) {
+static hipError_t launch_step_t(const StepArgs& h, hipStream_t st) {
   using T = typename IO::T;
-  const int64_t threads = a.batch * a.dim * 4;
+  StepDev<IO> a;
+  a.u = static_cast<const T*>(h.u); a.dlt = static_cast<const T*>(h.delta); a.A = h.A;
+  a.B = static_cast<const T*>(h.B); a.C = static_cast<const T*>(h.C); a.D = h.D;
+  a.z = static_cast<const T*>(h.z); a.bias = h.bias; a.state_in = h.state_in; a.state_out = h.state_out;
+  a.y = static_cast<T*>(h.y); a.conv_w = h.conv_w; a.conv_b = h.conv_b; a.cs_in = h.conv_state_in;
+  a.cs_out = h.conv_state_out; a.u_out = static_cast<T*>(h.u_out);
+  a.batch = h.batch; a.dim = h.dim; a.N = h.dstate; a.softplus = h.softplus; a.conv_k = h.conv_w ? h.conv_k : 0;
+  const int64_t threads = h.batch * h.dim * 4;
   const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
   auto run = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, static_cast<const T*>(a.u),
-                       static_cast<const T*>(a.delta), a.A, static_cast<const T*>(a.B), static_cast<const T*>(a.C),
-                       a.D, static_cast<const T*>(a.z), a.bias, a.state_in, a.state_out, static_cast<T*>(a.y),
-                       a.batch, a.dim, a.dstate, a.softplus);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
   };
-  if (a.dstate % 4 == 0) return run(ssm_step_kernel<IO, true>);
-  return run(ssm_step_kernel<IO, false>);
+  const bool vec4 = h.dstate % 4 == 0;
+  if (h.conv_w != nullptr) return vec4 ? run(ssm_step_kernel<IO, true, true>) : run(ssm_step_kernel<IO, false, true>);
+  return vec4 ? run(ssm_step_kernel<IO, true, false>) : run(ssm_step_kernel<IO, false, false>);
 }
 
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t st) {

@@ -189,3 +189,26 @@ def test_bwd_rejects_bad_arguments():
     assert call(sz=s2) == ssm.SSM_EUNSUPPORTED                      # dtype
     bad = list(base); bad[8] = 2
     assert call(bad) == ssm.SSM_EINVAL                              # softplus flag
+
+
+def test_step_conv_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    # x, conv_w, conv_b, K, cs_in, cs_out, delta, A, B, C, D, z, bias, softplus, state_in, state_out, y, u_out
+    base = [P(BIG), P(2 * BIG), None, 4, P(3 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), P(6 * BIG), P(7 * BIG),
+            None, None, None, 0, P(8 * BIG), P(8 * BIG), P(9 * BIG), None]
+    sizes = (8, 64, 16, 0, None)
+
+    def call(**kw):
+        idx = {"x": 0, "w": 1, "K": 3, "csi": 4, "cso": 5, "y": 16, "u": 17}
+        a = list(base)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return lib.ssm_step_conv(*a, *sizes)
+
+    assert call(w=None) == ssm.SSM_EINVAL                         # conv weights required
+    assert call(K=0) == ssm.SSM_EUNSUPPORTED and call(K=5) == ssm.SSM_EUNSUPPORTED
+    assert call(csi=None) == ssm.SSM_EINVAL                       # conv state needed for K > 1
+    assert call(cso=P(3 * BIG + 16)) == ssm.SSM_EINVAL            # partial conv-state overlap
+    assert call(u=P(9 * BIG)) == ssm.SSM_EINVAL                   # u_out on y
+    assert call(y=P(BIG)) == ssm.SSM_EINVAL                       # y on x

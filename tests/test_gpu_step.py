@@ -113,3 +113,67 @@ def test_decode_loop_equals_scan(dtype):
     torch.cuda.synchronize(DEV)
     assert rel_err(_host(state), _host(h_fwd)) <= 1e-4
     assert rel_err(_host(y_dec), _host(y_fwd)) <= TOL[dtype]
+
+
+# ------------------------------------------------------------ decode with the conv
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("K,inplace", [(4, True), (4, False), (3, True), (2, False), (1, True)])
+def test_step_conv_sequence_matches_conv_scan(K, inplace, dtype):
+    """T decode steps with the conv, from zero conv and SSM states, equal the
+    oracle's causal conv1d + SiLU followed by the scan over the same T steps;
+    the conv state ends holding the last K-1 inputs."""
+    b, d, n, T = 2, 40, 16, 12
+    inp = seq_inputs(b, d, n, T, dtype, seed=40 + K)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5 + K)
+    conv_w = torch.randn((d, K), generator=g, device=DEV) * (1.0 / K)
+    conv_b = torch.randn((d,), generator=g, device=DEV) * 0.1
+    cs = torch.zeros((b, d, K - 1), device=DEV) if K > 1 else None
+    state = torch.zeros((b, d, n), device=DEV)
+    ys, us = [], []
+    for t in range(T):
+        pick = lambda x: None if x is None else x[..., t].contiguous()
+        kw = dict(conv_b=conv_b, D=inp["D"], z=pick(inp["z"]), delta_bias=inp["delta_bias"], delta_softplus=True,
+                  return_u=True)
+        if not inplace:
+            kw["conv_state_out"] = torch.empty_like(cs) if cs is not None else None
+            kw["state_out"] = torch.empty_like(state)
+        y, cs2, st2, u = ssm.ssm_step_conv(pick(inp["u"]), conv_w, cs, pick(inp["delta"]), inp["A"],
+                                           pick(inp["B"]), pick(inp["C"]), state, **kw)
+        cs, state = cs2, st2
+        ys.append(y.clone())
+        us.append(u.clone())
+    torch.cuda.synchronize(DEV)
+    u_ref = ref.causal_conv1d(inp["u"], conv_w, conv_b)
+    y_ref, last_ref = ref.selective_scan_fwd(u_ref, inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                             inp["delta_bias"], True)
+    tol = TOL[dtype]
+    assert rel_err(np.stack([_host(v) for v in us], -1), u_ref) <= tol
+    assert rel_err(np.stack([_host(v) for v in ys], -1), y_ref) <= tol
+    assert rel_err(_host(state), last_ref) <= 1e-4
+    if K > 1:
+        x_host = inp["u"].float().cpu().numpy()
+        np.testing.assert_array_equal(_host(cs), x_host[:, :, T - (K - 1):])
+
+
+def test_step_conv_matches_conv_forward_on_gpu():
+    """Decode over T steps reproduces ssm_scan_fwd_conv's y and last state."""
+    b, d, n, T = 1, 64, 16, 40
+    inp = seq_inputs(b, d, n, T, torch.float32, seed=77)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    conv_w = torch.randn((d, 4), generator=g, device=DEV) * 0.25
+    y_fwd, last_fwd, _, _ = ssm.ssm_scan_fwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"],
+                                                  D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                                  delta_softplus=True)
+    cs = torch.zeros((b, d, 3), device=DEV)
+    state = torch.zeros((b, d, n), device=DEV)
+    for t in range(T):
+        pick = lambda x: x[..., t].contiguous()
+        y, cs, state, _ = ssm.ssm_step_conv(pick(inp["u"]), conv_w, cs, pick(inp["delta"]), inp["A"], pick(inp["B"]),
+                                            pick(inp["C"]), state, D=inp["D"], z=pick(inp["z"]),
+                                            delta_bias=inp["delta_bias"], delta_softplus=True)
+        assert rel_err(_host(y), _host(y_fwd[..., t])) <= 1e-5
+    torch.cuda.synchronize(DEV)
+    assert rel_err(_host(state), _host(last_fwd)) <= 1e-5
