@@ -275,13 +275,28 @@ def bwd_bench(args):
     inp = workloads.make_inputs(w, device=dev, seed=0)
     gr = workloads.make_grads(w, device=dev, seed=0)
     sc = args.bwd_state_chunk
-    _, _, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                                       inp["delta_bias"], delta_softplus=w.softplus, state_chunk=sc)
+    K = args.conv
+    if K:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        conv_w = torch.randn((w.dim, K), generator=g, device=dev) * (1.0 / K)
+        conv_b = torch.randn((w.dim,), generator=g, device=dev) * 0.1
+        _, _, cs, _ = ssm.ssm_scan_fwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"],
+                                            conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                            delta_softplus=w.softplus, state_chunk=sc)
 
-    def step():
-        ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, gr["dy"], D=inp["D"],
-                         z=inp["z"], delta_bias=inp["delta_bias"], delta_softplus=w.softplus, dlast=gr["dlast"],
-                         states_per_lane=args.states_per_lane)
+        def step():
+            ssm.ssm_scan_bwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, gr["dy"],
+                                  conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                  delta_softplus=w.softplus, dlast=gr["dlast"], states_per_lane=args.states_per_lane)
+    else:
+        _, _, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                           inp["z"], inp["delta_bias"], delta_softplus=w.softplus, state_chunk=sc)
+
+        def step():
+            ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, gr["dy"], D=inp["D"],
+                             z=inp["z"], delta_bias=inp["delta_bias"], delta_softplus=w.softplus, dlast=gr["dlast"],
+                             states_per_lane=args.states_per_lane)
 
     warm = max(3, args.warmup // 10)
     steps = max(1, args.steps // 4)
@@ -297,7 +312,7 @@ def bwd_bench(args):
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     ms = ev0.elapsed_time(ev1) / steps
-    bytes_alg = bwd_algorithmic_bytes(w, sc)
+    bytes_alg = bwd_algorithmic_bytes(w, sc) + (8 * w.dim * (K + 1) if K else 0)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     tflops = w.state_steps() * BWD_FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
     out = {
@@ -308,7 +323,7 @@ def bwd_bench(args):
         "data": "synthetic (seeded; shapes and value recipes of the workload)",
         "config": {"workload": w.name + "-bwd", "batch": w.batch, "d_inner": w.dim, "d_state": w.dstate,
                    "seq_len": w.L, "io_dtype": w.dtype, "gated": w.gated, "state_chunk": sc,
-                   "states_per_lane": args.states_per_lane},
+                   "states_per_lane": args.states_per_lane, **({"conv_k": K} if K else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(BWD_ALU_PEAK_TFLOPS, 2),

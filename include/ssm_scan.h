@@ -232,6 +232,33 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
                  int dtype, int states_per_lane, void *stream);
 
 /*
+ * ssm_scan_bwd_conv -- gradients of ssm_scan_fwd_conv (the causal conv1d +
+ * SiLU fused in front of the scan) by the same chunked recomputation as
+ * ssm_scan_bwd.  u = silu(pre) is recomputed from x; with du the scan's
+ * gradient of u (as ssm_scan_bwd computes it) and pre_t = conv_b +
+ * sum_k conv_w[k] x_{t-(K-1)+k}:
+ *     dpre_t = du_t silu'(pre_t),   silu'(p) = sig(p) (1 + p (1 - sig(p)))
+ *     dx_t   = sum_k conv_w[k] dpre_{t+(K-1)-k}          (dpre past L is zero)
+ *     dconv_w[d,k] = sum_{b,t} dpre_t x_{t-(K-1)+k},  dconv_b[d] = sum_{b,t} dpre_t
+ *   x, conv_w, conv_b, conv_k : as for ssm_scan_fwd_conv; chunk_states must
+ *                  come from ssm_scan_fwd_conv with the same inputs.
+ *   dx           : [batch, d_inner, L], dtype `dtype` (in place of du).
+ *   dconv_w      : [d_inner, conv_k] float32 output; dconv_b: [d_inner]
+ *                  float32 output, nullable.
+ * Other arguments, semantics (sums by float32 atomic adds) and errors as
+ * ssm_scan_bwd.
+ */
+int ssm_scan_bwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_k,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                      const float *h0, const float *chunk_states, int64_t state_chunk,
+                      const void *dy, const float *dlast,
+                      void *dx, float *dconv_w, float *dconv_b, void *ddelta, float *dA, float *dB, float *dC,
+                      float *dD, void *dz, float *ddelta_bias, float *dh0,
+                      int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                      int dtype, int states_per_lane, void *stream);
+
+/*
  * ssm_step -- one recurrent step of the selective scan for every (batch,
  * channel): the constant-time inference form of the recurrence
  * ([Mamba-2 page] §7; the step itself is [Scan page] §1.2):

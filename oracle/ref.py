@@ -55,6 +55,7 @@ __all__ = [
     "selective_scan_bruteforce",
     "selective_scan_bwd",
     "causal_conv1d",
+    "causal_conv1d_silu_bwd",
     "affine_scan",
     "lti_closed_form",
 ]
@@ -477,6 +478,35 @@ def causal_conv1d(x, w, b=None, activation: Optional[str] = "silu"):
     elif activation is not None:
         raise ValueError("activation must be 'silu' or None")
     return out
+
+
+def causal_conv1d_silu_bwd(x, w, b, du):
+    """Gradients through u = silu(causal_conv1d(x, w, b)) (the reading of
+    ``causal_conv1d``), float64, for an incoming gradient du of u:
+
+        pre_t   = b + sum_k w[k] x_{t-(K-1)+k}
+        dpre_t  = du_t * silu'(pre_t),  silu'(p) = sig(p) (1 + p (1 - sig(p)))
+        dx_t    = sum_k w[k] dpre_{t+(K-1)-k}      (terms past the end are zero)
+        dw[d,k] = sum_{b,t} dpre_t x_{t-(K-1)+k},  db[d] = sum_{b,t} dpre_t
+
+    Returns (dx [b,d,L], dw [d,K], db [d])."""
+    x = _f64(x)
+    w = _f64(w)
+    du = _f64(du)
+    bsz, dim, L = x.shape
+    K = w.shape[1]
+    pre = causal_conv1d(x, w, b, activation=None)
+    sig = 1.0 / (1.0 + np.exp(-pre))
+    dpre = du * sig * (1.0 + pre * (1.0 - sig))
+    dx = np.zeros_like(x)
+    dw = np.zeros((dim, K))
+    for k in range(K):
+        shift = K - 1 - k                 # w[:, k] multiplies x[t - shift]
+        if shift >= L:
+            continue
+        dx[:, :, :L - shift] += w[None, :, k, None] * dpre[:, :, shift:]
+        dw[:, k] = np.einsum("bdl,bdl->d", dpre[:, :, shift:], x[:, :, :L - shift])
+    return dx, dw, dpre.sum(axis=(0, 2))
 
 
 def lti_closed_form(a: float, b):

@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_step", "ssm_step_conv", "affine_scan", "affine_scan_order", "plan_for",
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_conv", "ssm_step", "ssm_step_conv", "affine_scan", "affine_scan_order", "plan_for",
            "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,9 @@ def load_library():
     lib.ssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, P, P, P, P, P, P, P, P, P, P, P,
                                  I64, I64, I64, I64, I, I, P]
     lib.ssm_scan_bwd.restype = I
+    lib.ssm_scan_bwd_conv.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, P, P, I64, P, P, P, P, P, P, P, P, P, P,
+                                      P, P, P, I64, I64, I64, I64, I, I, P]
+    lib.ssm_scan_bwd_conv.restype = I
     lib.ssm_step.restype = I
     lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
                                       ctypes.POINTER(I64)]
@@ -340,6 +343,65 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                               _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
                               _ptr(out["dh0"]), bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16,
                               int(states_per_lane), _stream(device))
+    _check(rc)
+    return out
+
+
+def ssm_scan_bwd_conv(x: torch.Tensor, conv_w: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                      B: torch.Tensor, C: torch.Tensor, chunk_states: torch.Tensor, state_chunk: int,
+                      dy: torch.Tensor, conv_b: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                      z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                      delta_softplus: bool = False, h0: Optional[torch.Tensor] = None,
+                      dlast: Optional[torch.Tensor] = None, states_per_lane: int = 0) -> dict:
+    """Gradients of ssm_scan_fwd_conv (see ``ssm_scan_bwd_conv`` in
+    include/ssm_scan.h).  Returns a dict like ssm_scan_bwd with dx in place
+    of du, plus dconv_w [d, K] and dconv_b [d] (float32; dconv_b None when
+    conv_b is None)."""
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_bwd_conv needs CUDA/HIP tensors")
+    bsz, dim, L = x.shape
+    n = A.shape[1]
+    K = conv_w.shape[1]
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    for t, name, shape in ((x, "x", (bsz, dim, L)), (delta, "delta", (bsz, dim, L)), (B, "B", (bsz, n, L)),
+                           (C, "C", (bsz, n, L)), (dy, "dy", (bsz, dim, L))):
+        _need(t, name, dt, device, shape)
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(conv_w, "conv_w", torch.float32, device, (dim, K))
+    if state_chunk <= 0:
+        raise ValueError("state_chunk must be positive")
+    _need(chunk_states, "chunk_states", torch.float32, device, (bsz, -(-L // state_chunk), dim, n))
+    for t, name in ((conv_b, "conv_b"), (D, "D"), (delta_bias, "delta_bias")):
+        if t is not None:
+            _need(t, name, torch.float32, device, (dim,))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    for t, name in ((h0, "h0"), (dlast, "dlast")):
+        if t is not None:
+            _need(t, name, torch.float32, device, (bsz, dim, n))
+    f32 = dict(device=device, dtype=torch.float32)
+    out = {
+        "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dconv_w": torch.empty((dim, K), **f32),
+        "dconv_b": torch.empty((dim,), **f32) if conv_b is not None else None,
+        "dA": torch.empty((dim, n), **f32), "dB": torch.empty((bsz, n, L), **f32),
+        "dC": torch.empty((bsz, n, L), **f32), "dD": torch.empty((dim,), **f32),
+        "ddelta_bias": torch.empty((dim,), **f32), "dh0": torch.empty((bsz, dim, n), **f32),
+    }
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_bwd_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), int(K), _ptr(delta), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                   _ptr(chunk_states), int(state_chunk), _ptr(dy), _ptr(dlast), _ptr(out["dx"]),
+                                   _ptr(out["dconv_w"]), _ptr(out["dconv_b"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                                   _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                                   _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), bsz, dim, n, L,
+                                   SSM_F32 if dt == torch.float32 else SSM_BF16, int(states_per_lane),
+                                   _stream(device))
     _check(rc)
     return out
 

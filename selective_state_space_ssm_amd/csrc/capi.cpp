@@ -324,12 +324,17 @@ int ssm_step(const void* u, const void* delta, const float* A, const void* B, co
   return SSM_OK;
 }
 
-int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                 const void* z, const float* delta_bias, int delta_softplus, const float* h0,
-                 const float* chunk_states, int64_t state_chunk, const void* dy, const float* dlast, void* du,
-                 void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int states_per_lane,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                  const float* chunk_states, int64_t state_chunk, const void* dy, const float* dlast, void* du,
+                  void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                  int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int states_per_lane,
+                  const float* conv_w, const float* conv_b, int conv_k, float* dconv_w, float* dconv_b,
+                  void* stream) {
   g_err.clear();
   if (!u || !delta || !A || !B || !C || !chunk_states || !dy || !du || !ddelta || !dA || !dB || !dC)
     return fail(SSM_EINVAL, "u, delta, A, B, C, chunk_states, dy, du, ddelta, dA, dB and dC must not be NULL");
@@ -342,8 +347,11 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                 ssm::rows_time_tile(), ssm::kBwdMaxChunk, (long long)state_chunk);
   if (states_per_lane != 0 && states_per_lane != 1 && states_per_lane != 2 && states_per_lane != 4)
     return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", states_per_lane);
+  if (conv_w != nullptr && (conv_k < 1 || conv_k > 4))
+    return fail(SSM_EUNSUPPORTED, "conv_k must be 1 to 4 (got %d)", conv_k);
+  if (conv_w != nullptr && dconv_w == nullptr) return fail(SSM_EINVAL, "dconv_w must not be NULL");
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, chunk_states, dy, dlast,
-                        du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0};
+                        du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, conv_w, conv_b, dconv_w, dconv_b};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
   const uint64_t es = dtype == SSM_F32 ? 4 : 2;
@@ -354,11 +362,14 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                        range_of(dy, nbdl * es), range_of(B, nbnl * es), range_of(C, nbnl * es),
                        range_of(A, ndn * 4), range_of(D, uint64_t(d_inner) * 4),
                        range_of(delta_bias, uint64_t(d_inner) * 4), range_of(h0, nbdn * 4),
-                       range_of(chunk_states, K * nbdn * 4), range_of(dlast, nbdn * 4)};
+                       range_of(chunk_states, K * nbdn * 4), range_of(dlast, nbdn * 4),
+                       range_of(conv_w, uint64_t(d_inner) * (conv_w ? conv_k : 0) * 4),
+                       range_of(conv_b, uint64_t(d_inner) * 4)};
   const Range rout[] = {range_of(du, nbdl * es), range_of(ddelta, nbdl * es), range_of(dz, nbdl * es),
                         range_of(dA, ndn * 4), range_of(dB, nbnl * 4), range_of(dC, nbnl * 4),
                         range_of(dD, uint64_t(d_inner) * 4), range_of(ddelta_bias, uint64_t(d_inner) * 4),
-                        range_of(dh0, nbdn * 4)};
+                        range_of(dh0, nbdn * 4), range_of(dconv_w, uint64_t(d_inner) * (conv_w ? conv_k : 0) * 4),
+                        range_of(dconv_b, uint64_t(d_inner) * 4)};
   for (size_t i = 0; i < sizeof(rout) / sizeof(rout[0]); ++i) {
     for (const Range& r : rin)
       if (overlap(rout[i], r)) return fail(SSM_EINVAL, "gradient outputs must not overlap any input");
@@ -366,13 +377,18 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
       if (overlap(rout[i], rout[j])) return fail(SSM_EINVAL, "gradient outputs must not overlap each other");
   }
   const int64_t groups = batch * ceil_div(d_inner, kGroup);
-  const int S = states_per_lane != 0 ? states_per_lane : bwd_states_for(groups);
+  int S = states_per_lane != 0 ? states_per_lane : bwd_states_for(groups);
+  // with the conv in front, four states per lane run out of registers
+  // (spills) and LDS (occupancy): two measured faster at the 1.4B shape
+  if (states_per_lane == 0 && conv_w != nullptr && S == 4) S = 2;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = ssm::launch_zero(dA, int64_t(ndn), st);
   if (e == hipSuccess) e = ssm::launch_zero(dB, int64_t(nbnl), st);
   if (e == hipSuccess) e = ssm::launch_zero(dC, int64_t(nbnl), st);
   if (e == hipSuccess && dD) e = ssm::launch_zero(dD, d_inner, st);
   if (e == hipSuccess && ddelta_bias) e = ssm::launch_zero(ddelta_bias, d_inner, st);
+  if (e == hipSuccess && conv_w) e = ssm::launch_zero(dconv_w, d_inner * conv_k, st);
+  if (e == hipSuccess && conv_w && dconv_b) e = ssm::launch_zero(dconv_b, d_inner, st);
   if (e != hipSuccess) return hip_fail(e, "gradient clear launch");
   ssm::BwdArgs a{};
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
@@ -381,9 +397,39 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.dh0 = dh0;
   a.batch = batch; a.dim = d_inner; a.dstate = d_state; a.L = L; a.state_chunk = state_chunk;
   a.softplus = delta_softplus;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = conv_w ? conv_k : 0; a.dconv_w = dconv_w; a.dconv_b = dconv_b;
   e = ssm::launch_bwd(a, dtype == SSM_BF16, S, st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int delta_softplus, const float* h0,
+                 const float* chunk_states, int64_t state_chunk, const void* dy, const float* dlast, void* du,
+                 void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                 int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, int states_per_lane,
+                 void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_states, state_chunk, dy, dlast,
+                       du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, batch, d_inner, d_state, L, dtype,
+                       states_per_lane, nullptr, nullptr, 0, nullptr, nullptr, stream);
+}
+
+int ssm_scan_bwd_conv(const void* x, const float* conv_w, const float* conv_b, int conv_k, const void* delta,
+                      const float* A, const void* B, const void* C, const float* D, const void* z,
+                      const float* delta_bias, int delta_softplus, const float* h0, const float* chunk_states,
+                      int64_t state_chunk, const void* dy, const float* dlast, void* dx, float* dconv_w,
+                      float* dconv_b, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                      float* ddelta_bias, float* dh0, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                      int dtype, int states_per_lane, void* stream) {
+  g_err.clear();
+  if (!conv_w) return fail(SSM_EINVAL, "conv_w must not be NULL");
+  return scan_bwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_states, state_chunk, dy, dlast,
+                       dx, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, batch, d_inner, d_state, L, dtype,
+                       states_per_lane, conv_w, conv_b, conv_k, dconv_w, dconv_b, stream);
 }
 
 int ssm_step_conv(const void* x, const float* conv_w, const float* conv_b, int conv_k, const float* conv_state_in,

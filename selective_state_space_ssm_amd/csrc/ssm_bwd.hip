@@ -71,6 +71,7 @@ constexpr int kBT = kBwdTile;   // steps per tile (16: one DPP row of steps)
 constexpr int kCG = 16;         // channels per workgroup
 constexpr int kNS = 16;         // state slots per workgroup
 constexpr int kBR = kBT + 4;    // LDS row stride in floats (float4 rows, staggered banks)
+constexpr int kXR = kBR + 20;   // CONV: LDS row of pre (kBR) then x at steps -3 .. 15 (and padding)
 
 // DPP lane patterns within a row of 16 lanes (lane l reads the lane named)
 constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: l ^ 1
@@ -192,11 +193,16 @@ struct BwdDev {
   float* dD;
   float* dbias;
   float* dh0;
+  const float* convw;   // CONV: [d][K] conv1d weights (u then points at x, du at dx)
+  const float* convb;   // CONV: [d] nullable
+  float* dconvw;        // CONV: [d][K], accumulated
+  float* dconvb;        // CONV: [d] nullable, accumulated
 };
 
 struct BwdSz {
   int64_t batch, dim, dstate, L, sc;
   int softplus;
+  int convk;
 };
 
 }  // namespace
@@ -205,8 +211,15 @@ struct BwdSz {
 // 4/S wavefronts; grid (ceil(d_inner/16), batch).  With S <= 2 the tile's a_t
 // are kept in registers; with S = 4 they are recomputed on the way back (the
 // registers for them are not there).
-template <typename IO, int S, bool GATED, bool VEC>
-__global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz p) {
+// CONV: the scan's input is u = silu(pre), pre = conv_b + sum_j w4[j] x_{t-3+j}
+// (the causal conv1d in front, K <= 4 taps right-aligned in w4), recomputed
+// from x like the forward; the epilogue turns du into dpre = du silu'(pre),
+// adds dpre x into dconv_w and dpre into dconv_b, and leaves dpre in LDS;
+// dx_t = sum_j w4[j] dpre_{t+3-j} of a tile is formed after the next tile's
+// prep barrier, when the dpre of the tile and of the one after it (the
+// previous tile processed) are both in LDS.
+template <typename IO, int S, bool GATED, bool VEC, bool CONV>
+__global__ __launch_bounds__(256 / S, S == 1 ? 3 : 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz p) {
   using T = typename IO::T;
   using Buf = typename BufOf<IO>::type;
   constexpr int W = 4 / S;
@@ -226,7 +239,9 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   float* sGs = sDu + kCG * kBR;         // [16][kBR] gs
   float* sBC = sGs + kCG * kBR;         // [2][16 n][16 t] B then C
   float* sX = sBC + 2 * kNS * kBT;      // [W][3][16][kBR] four-row sums: s, r, w
-  float* sCk = sX + W * 3 * kCG * kBR;  // [tiles][16 n][16 c] tile start states
+  float* sDP = sX + W * 3 * kCG * kBR;  // CONV: [2][16][kBR] dpre of two consecutive tiles
+  float* sPX = sDP + (CONV ? 2 * kCG * kBR : 0);  // CONV: [2][16][kXR] pre (kBR) and x (3 + kBT) of a tile
+  float* sCk = sPX + (CONV ? 2 * kCG * kXR : 0);  // [tiles][16 n][16 c] tile start states
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,14 +315,22 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   // ---- raw words of one tile, loaded a tile ahead of their use
   constexpr int RW = VEC ? Buf::template kWords<V> : V;
   constexpr int BW = VEC ? Buf::template kWords<4> : 4;
+  constexpr int HW = CONV ? 3 : 1;  // conv halo: the 3 steps before the slot
   struct TileRegs {
     uint32_t wu[RW], wd[RW], wz[RW], wy[RW];
+    uint32_t wh[HW];
     uint32_t wbc[BCQ][BW];
   };
   // FULL: also z, dy and C (phase 2); otherwise u, delta and B only.
   auto load_tile = [&](TileRegs& R, int t0, auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if constexpr (CONV) {
+      // before step 0 of channel 0 the offset wraps past the resource and
+      // reads zero; the conv front zeroes the other steps before 0
+#pragma unroll
+      for (int j = 0; j < 3; ++j) Buf::template ldw<1>(rU, poff + toff - (3 - j) * ES, &R.wh[j]);
+    }
     if constexpr (VEC) {
       Buf::template ldw<V>(rU, poff + toff, R.wu);
       Buf::template ldw<V>(rD, poff + toff, R.wd);
@@ -356,11 +379,47 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     return make_float4(v[0], v[1], v[2], v[3]);
   };
 
+  // ---- conv front (CONV): u = silu(pre) from x and the halo
+  float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cbias = 0.0f;
+  float dcw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dcb = 0.0f;
+  if constexpr (CONV) {
+    const int Kc = p.convk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (pvalid && j >= 4 - Kc) w4[j] = a.convw[pd * Kc + (j - (4 - Kc))];
+    cbias = (pvalid && a.convb != nullptr) ? a.convb[pd] : 0.0f;
+  }
+  // xs[0..V+2] = x at steps pt-3 .. pt+V-1 of the tile; ru <- u, pre kept
+  auto conv_front = [&](TileRegs& R, int t0, float* ru, float* xs, float* pre) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      float v;
+      Buf::template unpack<1>(&R.wh[j], &v);
+      xs[j] = (t0 + pt - 3 + j >= 0) ? v : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) xs[3 + e] = ru[e];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float pr = cbias;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr = __builtin_fmaf(w4[j], xs[e + j], pr);
+      pre[e] = pr;
+      ru[e] = silu(pr);
+    }
+  };
+
   // ---- phase-1 prep: Delta2 and Delta*u of a whole tile, and B, into LDS
-  auto prep1 = [&](TileRegs& R) {
+  auto prep1 = [&](TileRegs& R, int t0) {
     float ru[V], rd[V], dt[V], du[V];
     unpack(R.wu, ru);
     unpack(R.wd, rd);
+    if constexpr (CONV) {
+      float xs[V + 3], pre[V];
+      conv_front(R, t0, ru, xs, pre);
+    }
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       const float v2 = delta2(rd[e], bias2, softplus);
@@ -382,6 +441,20 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     unpack(R.wd, rd);
     unpack(R.wy, ry);
     if constexpr (GATED) unpack(R.wz, rz);
+    if constexpr (CONV) {
+      // pre and x of the tile go to LDS for the epilogue (slot by tile parity)
+      float xs[V + 3], pre[V];
+      conv_front(R, t0, ru, xs, pre);
+      float* row = sPX + ((t0 / kBT) & 1) * kCG * kXR + pc * kXR;
+#pragma unroll
+      for (int e = 0; e < V; ++e) row[pt + e] = pre[e];
+#pragma unroll
+      for (int e = 0; e < V; ++e) row[kBR + 3 + pt + e] = xs[3 + e];
+      if (pt == 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) row[kBR + j] = xs[j];
+      }
+    }
     const bool full = t0 + kBT <= t_end;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -594,6 +667,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     }
     float odu[V], odd[V], odz[V];
     const bool full = t0 + kBT <= t_end;
+    float* dp = sDP + ((t0 / kBT) & 1) * kCG * kBR + pc * kBR + pt;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       const float sfull = __builtin_fmaf(Dd, eu[e], sv[e]);
@@ -605,22 +679,67 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
         dDacc = __builtin_fmaf(egs[e], eu[e], dDacc);
         dbacc += odd[e];
       }
+      if constexpr (CONV) {
+        // dpre = du silu'(pre), silu'(p) = sig(p) (1 + p (1 - sig(p))); zero past the end
+        const float* row = sPX + ((t0 / kBT) & 1) * kCG * kXR + pc * kXR;
+        const float pr = row[pt + e];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * pr));
+        const float dpr = (full || t0 + pt + e < t_end) ? odu[e] * (sg * (1.0f + pr * (1.0f - sg))) : 0.0f;
+        dp[e] = dpr;
+        dcb += dpr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dcw[j] = __builtin_fmaf(dpr, row[kBR + pt + e + j], dcw[j]);
+      }
     }
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
     if (VEC && full) {
-      Buf::template st<V>(rOU, poff + toff, odu);
+      if constexpr (!CONV) Buf::template st<V>(rOU, poff + toff, odu);
       Buf::template st<V>(rOD, poff + toff, odd);
       if constexpr (GATED) Buf::template st<V>(rOZ, poff + toff, odz);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e)
         if (t0 + pt + e < t_end) {
-          Buf::template st<1>(rOU, poff + toff + e * ES, &odu[e]);
+          if constexpr (!CONV) Buf::template st<1>(rOU, poff + toff + e * ES, &odu[e]);
           Buf::template st<1>(rOD, poff + toff + e * ES, &odd[e]);
           if constexpr (GATED) Buf::template st<1>(rOZ, poff + toff + e * ES, &odz[e]);
         }
     }
   };
+
+  // ---- dx of the tile at t0 (CONV): dx_t = sum_j w4[j] dpre_{t+3-j}, the
+  // dpre of this tile in its parity slot of sDP and of the tile after it in
+  // the other (zero after the end of the sequence)
+  auto conv_dx = [&](int t0) {
+    const float* cur = sDP + ((t0 / kBT) & 1) * kCG * kBR + pc * kBR;
+    const float* nxt = sDP + (((t0 / kBT) & 1) ^ 1) * kCG * kBR + pc * kBR;
+    float dv[V + 3];
+#pragma unroll
+    for (int e = 0; e < V + 3; ++e) {
+      const int q = pt + e;
+      dv[e] = q < kBT ? cur[q] : nxt[q - kBT];
+    }
+    float dx[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(w4[j], dv[e + 3 - j], acc);
+      dx[e] = acc;
+    }
+    const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if (VEC && t0 + kBT <= Li) {
+      Buf::template st<V>(rOU, poff + toff, dx);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (t0 + pt + e < Li) Buf::template st<1>(rOU, poff + toff + e * ES, &dx[e]);
+    }
+  };
+  if constexpr (CONV) {
+    for (int i = tid; i < 2 * kCG * kBR; i += NT) sDP[i] = 0.0f;
+  }
+  int prev_t0 = -1;
 
   // ---- chunks from last to first
   const int sc = static_cast<int>(p.sc);
@@ -662,7 +781,7 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
     // phase 1: states at the start of tiles 1 .. nt-1 (all full tiles)
 #pragma unroll 1
     for (int i = 0; i + 1 < nt; ++i) {
-      prep1(R);
+      prep1(R, cs + i * kBT);
       if (i + 2 < nt)
         load_tile(R, cs + (i + 1) * kBT, kPart{});
       else
@@ -683,13 +802,21 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
       else if (k > 0)
         load_tile(R, cs - sc, kPart{});
       __syncthreads();
+      if constexpr (CONV) {
+        if (prev_t0 >= 0) conv_dx(prev_t0);
+      }
       float hst[S];
 #pragma unroll
       for (int s = 0; s < S; ++s) hst[s] = myCk[(i * kNS + s) * kCG];
       compute(hst, t0, ce, k == 0 && i == 0);
       __syncthreads();
       epilogue(t0, ce);
+      prev_t0 = t0;
     }
+  }
+  if constexpr (CONV) {
+    __syncthreads();
+    conv_dx(prev_t0);
   }
 
   // ---- sums over batch rows and time: one atomic add per lane / thread
@@ -699,6 +826,13 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_bwd_kernel(BwdDev<IO> a, BwdSz
   if (pvalid) {
     if (a.dD != nullptr) unsafeAtomicAdd(a.dD + pd, dDacc);
     if (a.dbias != nullptr) unsafeAtomicAdd(a.dbias + pd, dbacc);
+    if constexpr (CONV) {
+      const int Kc = p.convk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j >= 4 - Kc) unsafeAtomicAdd(a.dconvw + pd * Kc + (j - (4 - Kc)), dcw[j]);
+      if (a.dconvb != nullptr) unsafeAtomicAdd(a.dconvb + pd, dcb);
+    }
   }
 }
 
@@ -707,13 +841,14 @@ __global__ __launch_bounds__(256) void ssm_zero_kernel(float* __restrict__ p, in
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
-size_t bwd_smem_bytes(int S, int64_t state_chunk) {
+size_t bwd_smem_bytes(int S, int64_t state_chunk, bool conv) {
   const int W = 4 / S;
   const int64_t tiles = (state_chunk + kBT - 1) / kBT;
-  return sizeof(float) * static_cast<size_t>(3 * kCG * kBR + 2 * kNS * kBT + W * 3 * kCG * kBR + tiles * kNS * kCG);
+  return sizeof(float) * static_cast<size_t>(3 * kCG * kBR + 2 * kNS * kBT + W * 3 * kCG * kBR +
+                                             (conv ? 2 * kCG * (kBR + kXR) : 0) + tiles * kNS * kCG);
 }
 
-template <typename IO, int S, bool GATED, bool VEC>
+template <typename IO, int S, bool GATED, bool VEC, bool CONV>
 static hipError_t launch_bwd_t(const BwdArgs& h, hipStream_t st) {
   using T = typename IO::T;
   BwdDev<IO> a;
@@ -738,18 +873,28 @@ static hipError_t launch_bwd_t(const BwdArgs& h, hipStream_t st) {
   a.dD = h.dD;
   a.dbias = h.dbias;
   a.dh0 = h.dh0;
-  const BwdSz p{h.batch, h.dim, h.dstate, h.L, h.state_chunk, h.softplus};
+  a.convw = h.conv_w;
+  a.convb = h.conv_b;
+  a.dconvw = h.dconv_w;
+  a.dconvb = h.dconv_b;
+  const BwdSz p{h.batch, h.dim, h.dstate, h.L, h.state_chunk, h.softplus, h.conv_w ? h.conv_k : 0};
   const dim3 grid(static_cast<unsigned>((h.dim + kCG - 1) / kCG), static_cast<unsigned>(h.batch));
-  hipLaunchKernelGGL((ssm_bwd_kernel<IO, S, GATED, VEC>), grid, dim3(256 / S), bwd_smem_bytes(S, h.state_chunk), st,
-                     a, p);
+  hipLaunchKernelGGL((ssm_bwd_kernel<IO, S, GATED, VEC, CONV>), grid, dim3(256 / S),
+                     bwd_smem_bytes(S, h.state_chunk, CONV), st, a, p);
   return hipGetLastError();
+}
+
+template <typename IO, int S, bool CONV>
+static hipError_t launch_bwd_c(const BwdArgs& h, hipStream_t st) {
+  const bool vec = h.L % 8 == 0;
+  if (h.z != nullptr)
+    return vec ? launch_bwd_t<IO, S, true, true, CONV>(h, st) : launch_bwd_t<IO, S, true, false, CONV>(h, st);
+  return vec ? launch_bwd_t<IO, S, false, true, CONV>(h, st) : launch_bwd_t<IO, S, false, false, CONV>(h, st);
 }
 
 template <typename IO, int S>
 static hipError_t launch_bwd_s(const BwdArgs& h, hipStream_t st) {
-  const bool vec = h.L % 8 == 0;
-  if (h.z != nullptr) return vec ? launch_bwd_t<IO, S, true, true>(h, st) : launch_bwd_t<IO, S, true, false>(h, st);
-  return vec ? launch_bwd_t<IO, S, false, true>(h, st) : launch_bwd_t<IO, S, false, false>(h, st);
+  return h.conv_w != nullptr ? launch_bwd_c<IO, S, true>(h, st) : launch_bwd_c<IO, S, false>(h, st);
 }
 
 hipError_t launch_bwd(const BwdArgs& h, bool bf16, int S, hipStream_t st) {

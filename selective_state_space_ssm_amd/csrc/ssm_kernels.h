@@ -108,10 +108,15 @@ struct BwdArgs {
   int64_t batch, dim, dstate, L;
   int64_t state_chunk;        // sc: multiple of the backward tile, at most kBwdMaxChunk
   int softplus;
+  const float* conv_w;        // nullable: [d][conv_k] conv1d in front (u then holds x, du receives dx)
+  const float* conv_b;        // [d] nullable
+  int conv_k;                 // 1..4
+  float* dconv_w;             // [d][conv_k], accumulated
+  float* dconv_b;             // [d] nullable, accumulated
 };
 constexpr int kBwdTile = 16;       // steps per backward tile
 constexpr int kBwdMaxChunk = 512;  // largest state_chunk (LDS holds one state per tile of a chunk)
-size_t bwd_smem_bytes(int S, int64_t state_chunk);
+size_t bwd_smem_bytes(int S, int64_t state_chunk, bool conv);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int S, hipStream_t st);
 // Fill n floats with zero (a kernel, not a memset).
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);

@@ -161,3 +161,49 @@ def test_bwd_full_size(name, sc):
     got = run_gpu(inp, sc)
     want = run_oracle(inp, use_c=True)
     check(got, want, w.torch_dtype, name)
+
+
+# ------------------------------------------------------- conv1d + SiLU in front
+
+CONV_CASES = [
+    # b, d, n, L, state_chunk, S, K
+    (1, 16, 16, 64, 32, 1, 4),
+    (2, 40, 16, 150, 64, 2, 4),
+    (2, 40, 16, 150, 64, 4, 3),
+    (1, 33, 16, 517, 128, 0, 2),
+    (2, 24, 8, 77, 32, 2, 1),
+    (1, 20, 16, 3, 32, 1, 4),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", CONV_CASES,
+                         ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}sc{c[4]}S{c[5]}K{c[6]}" for c in CONV_CASES])
+def test_bwd_conv_matches_oracle(case, dtype):
+    b, d, n, L, sc, S, K = case
+    inp = make(b, d, n, L, dtype, seed=50 + L + K)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9 + K)
+    conv_w = torch.randn((d, K), generator=g, device=DEV) * (1.0 / K)
+    conv_b = torch.randn((d,), generator=g, device=DEV) * 0.1
+    x = inp["u"]
+    _, _, cs, _ = ssm.ssm_scan_fwd_conv(x, conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], conv_b=conv_b,
+                                        D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                        delta_softplus=inp["delta_softplus"], h0=inp["h0"], state_chunk=sc)
+    got = ssm.ssm_scan_bwd_conv(x, conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, inp["dy"],
+                                conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                delta_softplus=inp["delta_softplus"], h0=inp["h0"], dlast=inp["dlast"],
+                                states_per_lane=S)
+    torch.cuda.synchronize(DEV)
+    u = ref.causal_conv1d(x, conv_w, conv_b)
+    want = ref.selective_scan_bwd(u, inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                                  delta_bias=inp["delta_bias"], delta_softplus=inp["delta_softplus"], h0=inp["h0"],
+                                  dy=inp["dy"], dlast=inp["dlast"])
+    dx, dw, db = ref.causal_conv1d_silu_bwd(x, conv_w, conv_b, want["du"])
+    want.update(dx=dx, dconv_w=dw, dconv_b=db)
+    for k in ("dx", "dconv_w", "dconv_b", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        if want.get(k) is None or got.get(k) is None:
+            continue
+        bound = 2e-2 if (dtype == torch.bfloat16 and k in ("dx", "ddelta", "dz")) else 1e-4
+        e = rel_err(_host(got[k]), want[k])
+        assert e <= bound, f"{case}: {k} rel err {e:.3g}"

@@ -7,7 +7,10 @@ oracle's ssm_oracle_bwd) against things other than itself:
   plain transcription of the forward recurrence of [Scan page] §1.2;
 * the closed form at L = 1 with a zero start state, where h = Delta B u and
   every gradient is a short product;
-* agreement of the C oracle with the NumPy one.
+* agreement of the C oracle with the NumPy one;
+* for the causal conv1d + SiLU in front (oracle.ref.causal_conv1d_silu_bwd):
+  central finite differences of the conv, and autograd through torch's
+  grouped conv1d composed with the forward transcription.
 
 The loss is sum(dy * y) + sum(dlast * last_state) throughout.
 """
@@ -171,3 +174,61 @@ def test_bwd_c_oracle_matches_numpy(gated, softplus, h0):
                 continue
             scale = max(1e-30, float(np.max(np.abs(v))))
             assert float(np.max(np.abs(got[k] - v))) / scale < 1e-12, (k, nth)
+
+
+# ------------------------------------------------------- conv1d + SiLU in front
+
+def _conv_loss(x, w, b, g):
+    return float(np.sum(g * ref.causal_conv1d(x, w, b)))
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_conv_bwd_matches_finite_differences(K):
+    rng = np.random.default_rng(30 + K)
+    x = rng.normal(size=(2, 3, 9))
+    w = rng.normal(size=(3, K))
+    b = rng.normal(size=3)
+    g = rng.normal(size=(2, 3, 9))
+    dx, dw, db = ref.causal_conv1d_silu_bwd(x, w, b, g)
+    eps = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (b, db)):
+        fd = np.empty_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = _conv_loss(x, w, b, g)
+            arr[idx] = old - eps
+            lm = _conv_loss(x, w, b, g)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert float(np.max(np.abs(grad - fd))) / max(1.0, float(np.max(np.abs(fd)))) < 1e-7
+
+
+def test_conv_then_scan_bwd_matches_autograd():
+    """The composed gradient (conv + SiLU, then the scan) against
+    torch.autograd through torch's grouped conv1d and a plain float64
+    transcription of the forward recurrence."""
+    rng = np.random.default_rng(33)
+    b, d, n, L, K = 2, 3, 4, 7, 4
+    p, dy, dlast, sp = _problem(34, b=b, d=d, n=n, L=L)
+    x = rng.normal(size=(b, d, L))
+    w = rng.normal(size=(d, K)) * 0.5
+    cb = rng.normal(size=d) * 0.1
+    u = ref.causal_conv1d(x, w, cb)
+    pp = dict(p)
+    pp["u"] = u
+    g = _grads(pp, dy, dlast, sp)
+    dx, dw, dcb = ref.causal_conv1d_silu_bwd(x, w, cb, g["du"])
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    bt = torch.tensor(cb, requires_grad=True)
+    ut = torch.nn.functional.silu(torch.nn.functional.conv1d(torch.nn.functional.pad(xt, (K - 1, 0)), wt[:, None, :],
+                                                             bt, groups=d))
+    t = {k: (None if v is None else torch.tensor(v, dtype=torch.float64)) for k, v in p.items()}
+    t["u"] = ut
+    y, last = _torch_forward(t, sp)
+    loss = (y * torch.tensor(dy)).sum() + (last * torch.tensor(dlast)).sum()
+    gx, gw, gb = torch.autograd.grad(loss, [xt, wt, bt])
+    np.testing.assert_allclose(dx, gx.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw, gw.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dcb, gb.numpy(), rtol=1e-10, atol=1e-12)
