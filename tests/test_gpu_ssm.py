@@ -239,3 +239,42 @@ def test_full_size_workload_sampled(name):
             assert rel_err(_host(last[bi, [0, 1, w.dim - 2, w.dim - 1]]), lt) <= 1e-4
     del inp, y, last
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ extreme values
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_extreme_values(S):
+    """delta spread over [-80, 80] (softplus's linear branch above 44 and a
+    step near zero far below), A as negative as -400 (decays that underflow
+    to zero within a step), and inputs of magnitude 1e3: the recurrence
+    stays finite and matches the oracle."""
+    inp = small_inputs(2, 32, 16, 300, seed=11)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(12)
+    inp["delta"] = (torch.rand(inp["delta"].shape, generator=g, device=DEV) * 160.0 - 80.0).contiguous()
+    inp["A"] = -torch.exp(torch.randn(inp["A"].shape, generator=g, device=DEV) * 2.0).clamp(max=400.0)
+    inp["u"] = (inp["u"] * 1e3).contiguous()
+    y, last = run_gpu(inp, plan="carry", states_per_lane=S)
+    assert torch.isfinite(y).all() and torch.isfinite(last).all()
+    y_ref, last_ref = oracle_all(inp)
+    assert rel_err(_host(y), y_ref) <= 1e-4
+    assert rel_err(_host(last), last_ref) <= 1e-4
+
+
+def test_nan_propagates_like_the_oracle():
+    """A NaN in u at one step of one channel makes that channel's outputs NaN
+    from that step on and nowhere else (each (b, d) row is an independent
+    recurrence); every other value matches the oracle."""
+    inp = small_inputs(1, 32, 16, 200, seed=13)
+    u = inp["u"].clone()
+    u[0, 5, 120] = float("nan")
+    inp["u"] = u
+    y, last = run_gpu(inp)
+    y_ref, last_ref = oracle_all(inp)
+    yg = _host(y)
+    np.testing.assert_array_equal(np.isnan(yg), np.isnan(y_ref))
+    assert np.isnan(yg[0, 5, 120:]).all() and not np.isnan(yg[0, 5, :120]).any()
+    ok = ~np.isnan(y_ref)
+    assert rel_err(yg[ok], y_ref[ok]) <= 1e-4
+    np.testing.assert_array_equal(np.isnan(_host(last)), np.isnan(last_ref))
