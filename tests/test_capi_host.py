@@ -71,6 +71,8 @@ BIG = 1 << 30
     (dict(S=3), ssm.SSM_EINVAL),
     (dict(chunk=100), ssm.SSM_EINVAL),
     (dict(u=BIG + 4), ssm.SSM_EINVAL),          # misaligned
+    (dict(L=((1 << 32) - 4096) // 64 + 1), ssm.SSM_EUNSUPPORTED),   # longest L + 1 (32-bit row offsets)
+    (dict(b=65536), ssm.SSM_EUNSUPPORTED),      # batch above the grid's y range
     (dict(y=BIG), ssm.SSM_EINVAL, ),             # placeholder replaced below
 ])
 def test_fwd_rejects_bad_arguments(kw, code):

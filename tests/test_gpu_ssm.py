@@ -278,3 +278,31 @@ def test_nan_propagates_like_the_oracle():
     ok = ~np.isnan(y_ref)
     assert rel_err(yg[ok], y_ref[ok]) <= 1e-4
     np.testing.assert_array_equal(np.isnan(_host(last)), np.isnan(last_ref))
+
+
+# ------------------------------------------------------------ large sizes
+
+def test_very_long_sequence_few_channels():
+    """b=1, d=16, L=2^22 (4.2M steps): the automatic plan splits L into
+    thousands of chunks (two-pass) and the per-row byte offsets reach 268 MB;
+    every channel's output against the C oracle."""
+    L = 1 << 22
+    inp = small_inputs(1, 16, 16, L, seed=21)
+    print(f"[long] L={L} plan {ssm.plan_for(1, 16, 16, L, 'f32')}", flush=True)
+    y, last = run_gpu(inp)
+    y_ref, last_ref = oracle_all(inp)
+    assert rel_err(_host(last), last_ref) <= 1e-4
+    assert rel_err(_host(y), y_ref) <= 1e-4
+    del inp, y, last
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("b,d,L", [(4096, 16, 64), (1, 16384, 128)], ids=["batch4096", "d16384"])
+def test_large_batch_or_width(b, d, L):
+    inp = small_inputs(b, d, 16, L, dtype=torch.bfloat16, seed=22)
+    y, last = run_gpu(inp)
+    rb, rd = _sample_rows(b, d, 64, seed=3)
+    y_ref, last_ref = oracle_rows(inp, rb, rd)
+    idx = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    assert rel_err(_host(y[idx]), y_ref) <= 2e-2
+    assert rel_err(_host(last[idx]), last_ref) <= 1e-4
