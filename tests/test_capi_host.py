@@ -214,3 +214,17 @@ def test_step_conv_rejects_bad_arguments():
     assert call(cso=P(3 * BIG + 16)) == ssm.SSM_EINVAL            # partial conv-state overlap
     assert call(u=P(9 * BIG)) == ssm.SSM_EINVAL                   # u_out on y
     assert call(y=P(BIG)) == ssm.SSM_EINVAL                       # y on x
+
+
+def test_autograd_wrappers_refuse_host_tensors():
+    """The autograd wrappers run only on the library: host tensors are
+    refused, never computed on the CPU."""
+    import torch
+    from selective_state_space_ssm_amd.autograd import selective_scan, selective_scan_conv
+    u = torch.zeros((1, 4, 8), requires_grad=True)
+    A = -torch.ones((4, 2))
+    B = torch.zeros((1, 2, 8))
+    with pytest.raises(ValueError, match="CUDA/HIP"):
+        selective_scan(u, u, A, B, B)
+    with pytest.raises(ValueError, match="CUDA/HIP"):
+        selective_scan_conv(u, torch.ones((4, 4)), None, u, A, B, B)
