@@ -56,6 +56,8 @@ __all__ = [
     "selective_scan_bwd",
     "causal_conv1d",
     "causal_conv1d_silu_bwd",
+    "out_proj",
+    "out_proj_tokens",
     "affine_scan",
     "lti_closed_form",
 ]
@@ -507,6 +509,36 @@ def causal_conv1d_silu_bwd(x, w, b, du):
         dx[:, :, :L - shift] += w[None, :, k, None] * dpre[:, :, shift:]
         dw[:, k] = np.einsum("bdl,bdl->d", dpre[:, :, shift:], x[:, :, :L - shift])
     return dx, dw, dpre.sum(axis=(0, 2))
+
+
+def out_proj(y, W):
+    """The Linear projection that closes the Mamba block after the gated
+    scan ([Mamba-2 page] §4.1 lists it last in the fused chain: Conv1D, SSM,
+    SiLU gate, Linear).  The pages give no shapes; the reading taken is the
+    usual Linear on every token's d_inner vector, with the weight stored
+    [d_model, d_inner], applied to y in the scan's [b, d_inner, L] layout and
+    written token-major:
+
+        out[b, t, m] = sum_k W[m, k] * y[b, k, t]
+
+    float64, one library matrix product per batch row.  Returns
+    [b, L, d_model]."""
+    y = _f64(y)
+    W = _f64(W)
+    out = np.empty((y.shape[0], y.shape[2], W.shape[0]))
+    for b in range(y.shape[0]):
+        out[b] = (W @ y[b]).T
+    return out
+
+
+def out_proj_tokens(y, W, bt):
+    """``out_proj`` for a list of (batch row, step) pairs only: row i of the
+    result is out[bt[i][0], bt[i][1], :] (the same definition, for sampled
+    outputs of large problems)."""
+    y = _f64(y) if isinstance(y, np.ndarray) else y
+    W = _f64(W)
+    cols = np.stack([_f64(y[b, :, t]) for b, t in bt])     # [n, d_inner]
+    return cols @ W.T
 
 
 def lti_closed_form(a: float, b):

@@ -430,3 +430,55 @@ def test_causal_conv1d_single_tap_is_pointwise():
     w = rng.normal(size=(4, 1))
     got = ref.causal_conv1d(x, w, None, activation=None)
     np.testing.assert_allclose(got, x * w[None, :, :], rtol=0, atol=0)
+
+
+# ------------------------------------------------------------ out projection
+
+def test_out_proj_matches_bruteforce_in_exact_arithmetic():
+    """out[b, t, m] = sum_k W[m, k] y[b, k, t], summed term by term in exact
+    rationals over small integers (so the float64 product is exact too).
+    Non-square W and distinct b, d_inner, L, d_model catch a transposed
+    operand or a swapped index."""
+    rng = random.Random(5)
+    bsz, dk, L, dm = 2, 5, 3, 4
+    y = np.array([[[rng.randint(-9, 9) for _ in range(L)] for _ in range(dk)] for _ in range(bsz)], dtype=float)
+    W = np.array([[rng.randint(-9, 9) for _ in range(dk)] for _ in range(dm)], dtype=float)
+    got = ref.out_proj(y, W)
+    assert got.shape == (bsz, L, dm)
+    for b in range(bsz):
+        for t in range(L):
+            for m in range(dm):
+                want = sum(Fraction(int(W[m, k])) * Fraction(int(y[b, k, t])) for k in range(dk))
+                assert Fraction(got[b, t, m]) == want, (b, t, m)
+
+
+def test_out_proj_identity_weight_is_the_token_major_transpose():
+    """W = I (d_model = d_inner): out[b, t, :] is y[b, :, t] exactly."""
+    y = np.random.default_rng(1).standard_normal((3, 6, 7))
+    out = ref.out_proj(y, np.eye(6))
+    assert np.array_equal(out, y.transpose(0, 2, 1))
+
+
+def test_out_proj_selector_rows_pick_channels():
+    """A one-hot row of W copies one channel's sequence; a row of ones sums
+    the channels (the column sum of y at every step)."""
+    y = np.random.default_rng(2).standard_normal((2, 5, 9))
+    W = np.zeros((3, 5))
+    W[0, 3] = 1.0
+    W[1, 0] = 1.0
+    W[2, :] = 1.0
+    out = ref.out_proj(y, W)
+    assert np.array_equal(out[:, :, 0], y[:, 3, :])
+    assert np.array_equal(out[:, :, 1], y[:, 0, :])
+    np.testing.assert_allclose(out[:, :, 2], y.sum(axis=1), rtol=1e-14, atol=1e-14)
+
+
+def test_out_proj_tokens_agrees_with_full_projection():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((2, 16, 11))
+    W = rng.standard_normal((8, 16))
+    full = ref.out_proj(y, W)
+    pairs = [(0, 0), (1, 10), (0, 5), (1, 3)]
+    got = ref.out_proj_tokens(y, W, pairs)
+    for i, (b, t) in enumerate(pairs):
+        np.testing.assert_allclose(got[i], full[b, t], rtol=1e-14, atol=1e-13)
