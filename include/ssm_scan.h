@@ -308,6 +308,27 @@ int ssm_step_conv(const void *x, const float *conv_w, const float *conv_b, int c
                   int64_t batch, int64_t d_inner, int64_t d_state, int dtype, void *stream);
 
 /*
+ * ssm_out_proj -- the Linear projection after the gated scan, the last
+ * operator of the fused chain ([Mamba-2 page] §4.1: Conv1D, SSM, SiLU gate,
+ * Linear), on the matrix cores:
+ *     out[b, t, m] = sum_k W[m, k] * y[b, k, t]
+ * with float32 accumulation.  y is read in the layout the scan writes; the
+ * result is token-major.
+ *   y     : [batch, d_inner, L], dtype `dtype` (the scan's y).
+ *   W     : [d_model, d_inner], dtype `dtype` (a Linear layer's weight).
+ *   out   : [batch, L, d_model], dtype `dtype`, output (bfloat16 rounded to
+ *           nearest even from the float32 sum); must not overlap y or W.
+ * Sizes: all positive; each of y's batch rows, W and each of out's batch
+ * rows must be under 2^31 bytes (else SSM_EUNSUPPORTED).  Any d_inner, L and
+ * d_model are accepted; the fastest path needs d_inner and L multiples of 8
+ * (bfloat16) or 4 (float32) and d_model a multiple of 4.
+ * Errors: SSM_EINVAL (NULL pointer, size <= 0, misalignment, overlap),
+ * SSM_EUNSUPPORTED (dtype, sizes), SSM_EHIP (launch).
+ */
+int ssm_out_proj(const void *y, const void *W, void *out, int64_t batch, int64_t d_inner, int64_t d_model,
+                 int64_t L, int dtype, void *stream);
+
+/*
  * affine_scan -- inclusive scan of affine pairs along each row
  * ([Scan page] §1.2 and §2.1; [Mamba-2 page] §2.2).
  * A pair (a, b) is the map h -> a*h + b; composition, later step first, is

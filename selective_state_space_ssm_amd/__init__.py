@@ -16,8 +16,9 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd", "ssm_scan_bwd_conv", "ssm_step", "ssm_step_conv", "affine_scan", "affine_scan_order", "plan_for",
-           "library_path", "load_library", "PLANS"]
+__all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd",
+           "ssm_scan_bwd_conv", "ssm_step", "ssm_step_conv", "ssm_out_proj", "affine_scan", "affine_scan_order",
+           "plan_for", "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -75,6 +76,8 @@ def load_library():
     lib.ssm_scan_plan_for.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(I), ctypes.POINTER(I),
                                       ctypes.POINTER(I64)]
     lib.ssm_scan_plan_for.restype = I
+    lib.ssm_out_proj.argtypes = [P, P, P, I64, I64, I64, I64, I, P]
+    lib.ssm_out_proj.restype = I
     lib.affine_scan.argtypes = [P, P, P, P, I64, I64, P]
     lib.affine_scan.restype = I
     lib.affine_scan_order.argtypes = [ctypes.POINTER(I)] * 4
@@ -505,6 +508,36 @@ def ssm_step_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_state: Optional[to
                                SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
     _check(rc)
     return y, conv_state_out, state_out, u
+
+
+def ssm_out_proj(y: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Linear projection after the gated scan (see ``ssm_out_proj`` in
+    include/ssm_scan.h): out[b, t, m] = sum_k W[m, k] * y[b, k, t].
+
+    y: [b, d_inner, L] (the scan's output), W: [d_model, d_inner], both
+    float32 or both bfloat16.  Returns out [b, L, d_model] in their dtype."""
+    device = y.device
+    if device.type != "cuda":
+        raise ValueError("ssm_out_proj needs CUDA/HIP tensors")
+    if y.dim() != 3 or W.dim() != 2:
+        raise ValueError("y must be [b, d_inner, L] and W [d_model, d_inner]")
+    bsz, dk, L = y.shape
+    dm = W.shape[0]
+    dt = y.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    _need(y, "y", dt, device, (bsz, dk, L))
+    _need(W, "W", dt, device, (dm, dk))
+    if out is None:
+        out = torch.empty((bsz, L, dm), device=device, dtype=dt)
+    else:
+        _need(out, "out", dt, device, (bsz, L, dm))
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_out_proj(_ptr(y), _ptr(W), _ptr(out), bsz, dk, dm, L,
+                              SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
+    _check(rc)
+    return out
 
 
 def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,

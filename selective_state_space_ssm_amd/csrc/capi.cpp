@@ -485,6 +485,35 @@ int ssm_step_conv(const void* x, const float* conv_w, const float* conv_b, int c
   return SSM_OK;
 }
 
+int ssm_out_proj(const void* y, const void* W, void* out, int64_t batch, int64_t d_inner, int64_t d_model,
+                 int64_t L, int dtype, void* stream) {
+  g_err.clear();
+  if (!y || !W || !out) return fail(SSM_EINVAL, "y, W and out must not be NULL");
+  if (batch <= 0 || d_inner <= 0 || d_model <= 0 || L <= 0)
+    return fail(SSM_EINVAL, "sizes must be positive (batch=%lld d_inner=%lld d_model=%lld L=%lld)",
+                (long long)batch, (long long)d_inner, (long long)d_model, (long long)L);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  const void* ptrs[] = {y, W, out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const int64_t es = dtype == SSM_F32 ? 4 : 2;
+  const int64_t lim = int64_t(1) << 31;
+  int64_t yrow, wsz, orow, tmp;
+  if (!mul_ok(d_inner, L, &tmp) || !mul_ok(tmp, es, &yrow) || yrow >= lim || !mul_ok(d_model, d_inner, &tmp) ||
+      !mul_ok(tmp, es, &wsz) || wsz >= lim || !mul_ok(L, d_model, &tmp) || !mul_ok(tmp, es, &orow) || orow >= lim)
+    return fail(SSM_EUNSUPPORTED, "a batch row of y or out, or W, reaches 2^31 bytes");
+  int64_t ybytes, obytes;
+  if (!mul_ok(yrow, batch, &ybytes) || !mul_ok(orow, batch, &obytes)) return fail(SSM_EINVAL, "tensor sizes overflow");
+  if (ssm::proj_tiles(dtype == SSM_BF16, batch, d_model, L) >= lim)
+    return fail(SSM_EUNSUPPORTED, "too many output tiles for one launch");
+  const Range ry = range_of(y, uint64_t(ybytes)), rw = range_of(W, uint64_t(wsz)), ro = range_of(out, uint64_t(obytes));
+  if (overlap(ro, ry) || overlap(ro, rw)) return fail(SSM_EINVAL, "out must not overlap y or W");
+  ssm::ProjArgs a{y, W, out, batch, d_inner, d_model, L};
+  hipError_t e = ssm::launch_out_proj(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "out-projection launch");
+  return SSM_OK;
+}
+
 int affine_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t rows, int64_t L,
                 void* stream) {
   g_err.clear();

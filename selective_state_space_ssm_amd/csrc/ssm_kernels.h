@@ -129,4 +129,16 @@ constexpr int kAffChunk = kAffT * kAffLanes * kAffW;
 hipError_t launch_affine_scan(const float* a, const float* b, float* oa, float* ob, int64_t rows, int64_t L,
                               hipStream_t st);
 
+// Output projection out[b][t][m] = sum_k W[m][k] y[b][k][t] on the matrix
+// cores (bfloat16 or float32 storage, float32 accumulation).
+struct ProjArgs {
+  const void* y;     // [batch][d_inner][L]
+  const void* w;     // [d_model][d_inner]
+  void* out;         // [batch][L][d_model]
+  int64_t batch, d_inner, d_model, L;
+};
+hipError_t launch_out_proj(const ProjArgs& a, bool bf16, hipStream_t st);
+// workgroups of one launch
+int64_t proj_tiles(bool bf16, int64_t batch, int64_t d_model, int64_t L);
+
 }  // namespace ssm

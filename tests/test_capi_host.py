@@ -228,3 +228,22 @@ def test_autograd_wrappers_refuse_host_tensors():
         selective_scan(u, u, A, B, B)
     with pytest.raises(ValueError, match="CUDA/HIP"):
         selective_scan_conv(u, torch.ones((4, 4)), None, u, A, B, B)
+
+
+def test_out_proj_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    y, w, out = P(BIG), P(2 * BIG), P(3 * BIG)
+
+    def call(y=y, w=w, out=out, b=2, k=64, m=32, L=128, dtype=ssm.SSM_BF16):
+        return lib.ssm_out_proj(y, w, out, b, k, m, L, dtype, None)
+
+    assert call(y=None) == ssm.SSM_EINVAL
+    assert call(out=None) == ssm.SSM_EINVAL
+    assert call(k=0) == ssm.SSM_EINVAL and call(L=-1) == ssm.SSM_EINVAL
+    assert call(dtype=7) == ssm.SSM_EUNSUPPORTED
+    assert call(w=P(2 * BIG + 8)) == ssm.SSM_EINVAL                   # misaligned
+    assert call(out=P(BIG + 64)) == ssm.SSM_EINVAL                     # out inside y
+    assert call(k=1 << 16, L=1 << 15) == ssm.SSM_EUNSUPPORTED          # a y row of 2^32 bytes
+    assert call(m=1 << 20, k=1 << 11) == ssm.SSM_EUNSUPPORTED          # W of 2^32 bytes
+    assert "2^31" in lib.ssm_last_error().decode()

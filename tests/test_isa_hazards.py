@@ -21,7 +21,7 @@ CSRC = os.path.join(ROOT, "selective_state_space_ssm_amd", "csrc")
 pytestmark = pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not available")
 
 
-SOURCES = ["ssm_fwd.hip", "ssm_bwd.hip", "ssm_step.hip", "affine_scan.hip"]
+SOURCES = ["ssm_fwd.hip", "ssm_bwd.hip", "ssm_step.hip", "ssm_proj.hip", "affine_scan.hip"]
 
 
 def _compile(tmp_dir, src):

@@ -157,3 +157,24 @@ def make_grads(w: Workload, device="cpu", seed: int = 0) -> dict:
     dy = torch.randn((w.batch, w.dim, w.L), generator=g, **f32).to(w.torch_dtype).contiguous()
     dlast = torch.randn((w.batch, w.dim, w.dstate), generator=g, **f32)
     return dict(dy=dy, dlast=dlast)
+
+
+def d_model_of(w: Workload) -> int:
+    """Model width of workload ``w``'s layer: d_inner / 2 (Mamba's expand = 2;
+    768 for 130m, 2048 for 1.4b)."""
+    return w.dim // 2
+
+
+def make_proj_inputs(batch: int, d_inner: int, d_model: int, L: int, dtype=torch.float32, device="cpu",
+                     seed: int = 0) -> dict:
+    """Inputs of the output projection: y ~ N(0,1) [batch, d_inner, L] (the
+    scan's output layout) and W ~ N(0,1)/sqrt(d_inner) [d_model, d_inner] (a
+    Linear weight at its usual scale), drawn in that order in float32 with a
+    generator seeded with ``seed + 2000`` and cast to ``dtype``."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 2000)
+    f32 = dict(device=dev, dtype=torch.float32)
+    y = torch.randn((batch, d_inner, L), generator=g, **f32).to(dtype).contiguous()
+    W = (torch.randn((d_model, d_inner), generator=g, **f32) / math.sqrt(d_inner)).to(dtype).contiguous()
+    return dict(y=y, W=W)
