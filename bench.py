@@ -70,6 +70,9 @@ def parse():
                         "(the workload's u is taken as the conv input x)")
     p.add_argument("--conv-u-out", action="store_true",
                    help="with --conv, also write u = silu(conv1d(x))")
+    p.add_argument("--out-proj", action="store_true",
+                   help="time the output projection after the scan (ssm_out_proj, matrix cores) at the "
+                        "workload's layer shape: d_inner -> d_model = d_inner / 2")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of the scan, time a plain device copy of COPY_BYTES (the reference "
                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -94,16 +97,25 @@ MEASURED_TRAFFIC = {
 }
 
 
-def kernel_digest() -> str:
-    """sha256 over the source of the forward scan kernels and the compiler
-    flags they are built with: a stored traffic figure holds only for the
-    build it was counted on."""
+# The same for the output projection kernel (ssm_proj.hip).
+MEASURED_PROJ_TRAFFIC = {
+    "130m": {"digest": "50f4f7a1d420beb2", "fetch_bytes": 199024585, "write_bytes": 50334736,
+             "profile": "profiles/ssm_out_proj_kernel_130m_f32.md"},
+    "1.4b": {"digest": "50f4f7a1d420beb2", "fetch_bytes": 403493708, "write_bytes": 79215696,
+             "profile": "profiles/ssm_out_proj_kernel_1.4b_bf16.md"},
+}
+
+
+def kernel_digest(sources=("ssm_fwd.hip", "ssm_device.h")) -> str:
+    """sha256 over the source of the given kernels (default: the forward scan)
+    and the compiler flags they are built with: a stored traffic figure holds
+    only for the build it was counted on."""
     import hashlib
     pkg = os.path.join(ROOT, "selective_state_space_ssm_amd")
     sys.path.insert(0, ROOT)
     from selective_state_space_ssm_amd import build as _b
     h = hashlib.sha256()
-    for name in ("ssm_fwd.hip", "ssm_device.h"):
+    for name in sources:
         with open(os.path.join(pkg, "csrc", name), "rb") as f:
             h.update(f.read())
     h.update(" ".join(_b.FLAGS).encode())
@@ -336,6 +348,100 @@ def bwd_bench(args):
     print(json.dumps(out), flush=True)
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense matrix-core peaks
+
+
+def blas_threads() -> int:
+    """Threads NumPy's BLAS runs its matrix products on."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def proj_traffic(workload: str):
+    ent = MEASURED_PROJ_TRAFFIC.get(workload)
+    if not ent or ent["digest"] != kernel_digest(("ssm_proj.hip", "ssm_device.h")):
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
+
+
+def proj_bench(args):
+    """One ssm_out_proj launch per step: out[b, t, m] = sum_k W[m, k] y[b, k, t]
+    at the workload's layer (y [b, d_inner, L] in the scan's layout, W
+    [d_model, d_inner], d_model = d_inner / 2), inputs resident in HBM."""
+    import torch
+    import selective_state_space_ssm_amd as ssm
+    import workloads
+    from oracle import ref
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    dm = workloads.d_model_of(w)
+    inp = workloads.make_proj_inputs(w.batch, w.dim, dm, w.L, dtype=w.torch_dtype, device=dev, seed=0)
+    out = torch.empty((w.batch, w.L, dm), device=dev, dtype=w.torch_dtype)
+
+    def step():
+        ssm.ssm_out_proj(inp["y"], inp["W"], out=out)
+
+    warm = max(3, args.warmup // 10)
+    steps = max(1, args.steps // 4)
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev0.elapsed_time(ev1) / steps
+    flop = 2.0 * w.batch * w.L * dm * w.dim
+    tflops = flop / (ms * 1e-3) / 1e12
+    es = 4 if w.dtype == "f32" else 2
+    bytes_alg = es * (w.batch * w.dim * w.L + dm * w.dim + w.batch * w.L * dm)
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    res = {
+        "metric": "output projection TFLOP/s (2 b L d_model d_inner per launch)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16 (f32 accumulation)",
+        "data": "synthetic (seeded: y ~ N(0,1), W ~ N(0,1)/sqrt(d_inner))",
+        "config": {"workload": w.name + "-out-proj", "batch": w.batch, "seq_len": w.L, "d_inner": w.dim,
+                   "d_model": dm, "io_dtype": w.dtype},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": proj_traffic(w.name)},
+        "hbm_roofline": {"bound": "hbm", "achieved": round(bytes_alg / (ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "algorithmic_bytes": bytes_alg},
+    }
+    if args.cpu_seconds > 0:
+        # the oracle on whole tokens (every d_model output of a token), as many
+        # as fit the budget, scaled to TFLOP/s
+        import numpy as np
+        y_h = inp["y"].float().cpu().numpy().astype(np.float64)
+        W_h = inp["W"].float().cpu().numpy().astype(np.float64)
+        rng = np.random.default_rng(0)
+        n, spent = 16, 0.0
+        while True:
+            pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.L))) for _ in range(n)]
+            t0 = time.perf_counter()
+            ref.out_proj_tokens(y_h, W_h, pairs)
+            spent = time.perf_counter() - t0
+            if spent > args.cpu_seconds / 4 or n >= w.batch * w.L:
+                break
+            n *= 4
+        res["cpu_baseline"] = {"value": round(2.0 * n * dm * w.dim / spent / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} tokens x {dm} outputs (float64 NumPy matrix product)"}
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(inp, w, budget_s):
     """The float64 C oracle, as it is, on a bounded sample of whole channels
     of the same workload; throughput scaled to the workload's GB/s."""
@@ -388,6 +494,9 @@ def main():
         return
     if args.bwd:
         bwd_bench(args)
+        return
+    if args.out_proj:
+        proj_bench(args)
         return
     import torch
 

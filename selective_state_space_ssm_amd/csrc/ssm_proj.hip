@@ -234,33 +234,46 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int arow = wm * (BM / 2) + (lane & 15);
-  const int brow = wn * (BN / 2) + (lane & 15);
+  // MFMA operand reads.  Lane reads row (lane & 15) + 16 i of its wavefront's
+  // half at chunk 4 s + (lane >> 4).  With the swizzle above the chunk
+  // position of (step s, subtile i) is qpos ^ 4 s ^ 2 (i & 3), qpos a lane
+  // constant, so four per-lane byte offsets serve every read and the 16-row
+  // steps are immediate offsets.
   const int lgrp = lane >> 4;
+  int loff[4];
+  {
+    const int qpos = lgrp ^ (lane & 7) ^ ((lane >> 3) & 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) loff[x] = (lane & 15) * 128 + 16 * (qpos ^ (2 * x));
+  }
+  // both k-steps' fragments are read first (the reads overlap each other and
+  // the first MFMAs wait only for their own operands), then 2 x TI x TJ MFMAs
   auto compute = [&](int buf) {
-    const uint4* sw = lds + buf * (BM + BN) * 8;
-    const uint4* sy = sw + BM * 8;
+    const char* abase = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + wm * (BM / 2) * 128;
+    const char* bbase = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + BM * 128 + wn * (BN / 2) * 128;
+    uint4 fa[2][TI], fb[2][TJ];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int ch = s * 4 + lgrp;
-      uint4 a[TI], bv[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int row = arow + 16 * i;
-        a[i] = sw[row * 8 + (ch ^ swz(row))];
-      }
+      for (int i = 0; i < TI; ++i)
+        fa[s][i] = *reinterpret_cast<const uint4*>(abase + loff[((4 * s) ^ (2 * (i & 3))) >> 1] + 2048 * i);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = brow + 16 * j;
-        bv[j] = sy[row * 8 + (ch ^ swz(row))];
-      }
+      for (int j = 0; j < TJ; ++j)
+        fb[s][j] = *reinterpret_cast<const uint4*>(bbase + loff[((4 * s) ^ (2 * (j & 3))) >> 1] + 2048 * j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
       if constexpr (ES == 2) {
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i]), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[s][i]), as_bf16x8(fb[s][j]), acc[i][j],
+                                                                0, 0, 0);
       } else {
+        // the 16 k of a step: lane group g holds k = 4 g + e of its chunk;
+        // MFMA e takes element e of both operands (the same k on both sides)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -268,8 +281,8 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                  __uint_as_float(reinterpret_cast<const uint32_t*>(&a[i])[e]),
-                  __uint_as_float(reinterpret_cast<const uint32_t*>(&bv[j])[e]), acc[i][j], 0, 0, 0);
+                  __uint_as_float(reinterpret_cast<const uint32_t*>(&fa[s][i])[e]),
+                  __uint_as_float(reinterpret_cast<const uint32_t*>(&fb[s][j])[e]), acc[i][j], 0, 0, 0);
       }
     }
   };
