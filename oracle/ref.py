@@ -58,6 +58,7 @@ __all__ = [
     "causal_conv1d_silu_bwd",
     "out_proj",
     "out_proj_tokens",
+    "out_proj_bwd",
     "affine_scan",
     "lti_closed_form",
 ]
@@ -539,6 +540,26 @@ def out_proj_tokens(y, W, bt):
     W = _f64(W)
     cols = np.stack([_f64(y[b, :, t]) for b, t in bt])     # [n, d_inner]
     return cols @ W.T
+
+
+def out_proj_bwd(y, W, dout):
+    """Gradients of ``out_proj`` for an incoming gradient dout [b, L, d_model]
+    of its output, float64 (the chain rule of a linear map, one library
+    matrix product per term):
+
+        dy[b, k, t] = sum_m W[m, k] * dout[b, t, m]
+        dW[m, k]    = sum_{b, t} dout[b, t, m] * y[b, k, t]
+
+    Returns (dy [b, d_inner, L], dW [d_model, d_inner])."""
+    y = _f64(y)
+    W = _f64(W)
+    dout = _f64(dout)
+    dy = np.empty_like(y)
+    dW = np.zeros_like(W)
+    for b in range(y.shape[0]):
+        dy[b] = W.T @ dout[b].T
+        dW += dout[b].T @ y[b].T
+    return dy, dW
 
 
 def lti_closed_form(a: float, b):

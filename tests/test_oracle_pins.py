@@ -482,3 +482,42 @@ def test_out_proj_tokens_agrees_with_full_projection():
     got = ref.out_proj_tokens(y, W, pairs)
     for i, (b, t) in enumerate(pairs):
         np.testing.assert_allclose(got[i], full[b, t], rtol=1e-14, atol=1e-13)
+
+
+def test_out_proj_bwd_matches_central_differences():
+    """The gradients of the loss sum(out_proj(y, W) * R) by central
+    differences of the forward oracle (exact for a bilinear map up to
+    rounding), element by element on a tiny non-square case."""
+    rng = np.random.default_rng(11)
+    bsz, dk, L, dm = 2, 3, 4, 5
+    y = rng.standard_normal((bsz, dk, L))
+    W = rng.standard_normal((dm, dk))
+    R = rng.standard_normal((bsz, L, dm))
+    dy, dW = ref.out_proj_bwd(y, W, R)
+    loss = lambda yy, WW: float(np.sum(ref.out_proj(yy, WW) * R))
+    eps = 1e-3
+    for idx in np.ndindex(y.shape):
+        e = np.zeros_like(y)
+        e[idx] = eps
+        fd = (loss(y + e, W) - loss(y - e, W)) / (2 * eps)
+        assert abs(fd - dy[idx]) <= 1e-9 * max(1.0, abs(fd)), idx
+    for idx in np.ndindex(W.shape):
+        e = np.zeros_like(W)
+        e[idx] = eps
+        fd = (loss(y, W + e) - loss(y, W - e)) / (2 * eps)
+        assert abs(fd - dW[idx]) <= 1e-9 * max(1.0, abs(fd)), idx
+
+
+def test_out_proj_bwd_adjoint_identities():
+    """For the bilinear map out = P(y, W): <P(y, W), R> = <y, dy(R)> =
+    <W, dW(R)>, exactly in rationals over small integers (a transposed
+    or swapped term breaks one of them)."""
+    rng = random.Random(12)
+    bsz, dk, L, dm = 2, 3, 4, 5
+    y = np.array([[[rng.randint(-5, 5) for _ in range(L)] for _ in range(dk)] for _ in range(bsz)], dtype=float)
+    W = np.array([[rng.randint(-5, 5) for _ in range(dk)] for _ in range(dm)], dtype=float)
+    R = np.array([[[rng.randint(-5, 5) for _ in range(dm)] for _ in range(L)] for _ in range(bsz)], dtype=float)
+    dy, dW = ref.out_proj_bwd(y, W, R)
+    lhs = int(np.sum(ref.out_proj(y, W) * R))
+    assert int(np.sum(y * dy)) == lhs
+    assert int(np.sum(W * dW)) == lhs
