@@ -99,10 +99,10 @@ MEASURED_TRAFFIC = {
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "50f4f7a1d420beb2", "fetch_bytes": 199024585, "write_bytes": 50334736,
-             "profile": "profiles/ssm_out_proj_kernel_130m_f32.md"},
-    "1.4b": {"digest": "50f4f7a1d420beb2", "fetch_bytes": 403493708, "write_bytes": 79215696,
-             "profile": "profiles/ssm_out_proj_kernel_1.4b_bf16.md"},
+    "130m": {"digest": "94bbcc5602b20956", "fetch_bytes": 187067505, "write_bytes": 50337168,
+             "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
+    "1.4b": {"digest": "94bbcc5602b20956", "fetch_bytes": 404032254, "write_bytes": 82881544,
+             "profile": "profiles/ssm_proj_gemm_kernel_out_proj_1.4b_bf16.md"},
 }
 
 
@@ -383,9 +383,16 @@ def proj_bench(args):
     dm = workloads.d_model_of(w)
     inp = workloads.make_proj_inputs(w.batch, w.dim, dm, w.L, dtype=w.torch_dtype, device=dev, seed=0)
     out = torch.empty((w.batch, w.L, dm), device=dev, dtype=w.torch_dtype)
+    if args.bwd:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        dout = torch.randn((w.batch, w.L, dm), generator=g, device=dev).to(w.torch_dtype).contiguous()
 
-    def step():
-        ssm.ssm_out_proj(inp["y"], inp["W"], out=out)
+        def step():
+            ssm.ssm_out_proj_bwd(inp["y"], inp["W"], dout)
+    else:
+        def step():
+            ssm.ssm_out_proj(inp["y"], inp["W"], out=out)
 
     warm = max(3, args.warmup // 10)
     steps = max(1, args.steps // 4)
@@ -401,25 +408,27 @@ def proj_bench(args):
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     ms = ev0.elapsed_time(ev1) / steps
-    flop = 2.0 * w.batch * w.L * dm * w.dim
+    passes = 2 if args.bwd else 1          # backward: dy and dW, one contraction each
+    flop = 2.0 * w.batch * w.L * dm * w.dim * passes
     tflops = flop / (ms * 1e-3) / 1e12
     es = 4 if w.dtype == "f32" else 2
-    bytes_alg = es * (w.batch * w.dim * w.L + dm * w.dim + w.batch * w.L * dm)
+    bytes_alg = es * (w.batch * w.dim * w.L + dm * w.dim + w.batch * w.L * dm) * (5 if args.bwd else 3) // 3
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     res = {
-        "metric": "output projection TFLOP/s (2 b L d_model d_inner per launch)",
+        "metric": ("output projection backward TFLOP/s (dy and dW: 4 b L d_model d_inner per step)" if args.bwd
+                   else "output projection TFLOP/s (2 b L d_model d_inner per launch)"),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16 (f32 accumulation)",
         "data": "synthetic (seeded: y ~ N(0,1), W ~ N(0,1)/sqrt(d_inner))",
-        "config": {"workload": w.name + "-out-proj", "batch": w.batch, "seq_len": w.L, "d_inner": w.dim,
-                   "d_model": dm, "io_dtype": w.dtype},
+        "config": {"workload": w.name + ("-out-proj-bwd" if args.bwd else "-out-proj"), "batch": w.batch,
+                   "seq_len": w.L, "d_inner": w.dim, "d_model": dm, "io_dtype": w.dtype},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": proj_traffic(w.name)},
+                     "frac": round(tflops / peak, 4), "traffic": None if args.bwd else proj_traffic(w.name)},
         "hbm_roofline": {"bound": "hbm", "achieved": round(bytes_alg / (ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "algorithmic_bytes": bytes_alg},
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.bwd:
         # the oracle on whole tokens (every d_model output of a token), as many
         # as fit the budget, scaled to TFLOP/s
         import numpy as np
@@ -439,6 +448,24 @@ def proj_bench(args):
                                "cores": blas_threads(),
                                "kind": "oracle",
                                "sample": f"{n} tokens x {dm} outputs (float64 NumPy matrix product)"}
+    if args.cpu_seconds > 0 and args.bwd:
+        # the gradient oracle on the first Ls tokens of one batch row (dy of
+        # those tokens and their dW terms), Ls grown until it fills the budget
+        import numpy as np
+        y_h = inp["y"][:1].float().cpu().numpy().astype(np.float64)
+        W_h = inp["W"].float().cpu().numpy().astype(np.float64)
+        d_h = dout[:1].float().cpu().numpy().astype(np.float64)
+        ls = 16
+        while True:
+            t0 = time.perf_counter()
+            ref.out_proj_bwd(y_h[:, :, :ls], W_h, d_h[:, :ls, :])
+            spent = time.perf_counter() - t0
+            if spent > args.cpu_seconds / 4 or ls >= w.L:
+                break
+            ls = min(4 * ls, w.L)
+        res["cpu_baseline"] = {"value": round(4.0 * ls * dm * w.dim / spent / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{ls} tokens of one batch row: dy and dW terms (float64 NumPy)"}
     print(json.dumps(res), flush=True)
 
 
@@ -492,11 +519,11 @@ def main():
     if args.decode:
         decode_bench(args)
         return
-    if args.bwd:
-        bwd_bench(args)
-        return
     if args.out_proj:
         proj_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
     import torch
 

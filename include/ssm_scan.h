@@ -329,6 +329,30 @@ int ssm_out_proj(const void *y, const void *W, void *out, int64_t batch, int64_t
                  int64_t L, int dtype, void *stream);
 
 /*
+ * ssm_out_proj_bwd -- gradients of ssm_out_proj for an incoming gradient
+ * dout of its output (the chain rule of the same Linear), on the matrix
+ * cores with float32 accumulation:
+ *     dy[b, k, t] = sum_m W[m, k] * dout[b, t, m]
+ *     dW[m, k]    = sum_{b, t} dout[b, t, m] * y[b, k, t]
+ *   y     : [batch, d_inner, L], dtype `dtype` (the forward's input).
+ *   W     : [d_model, d_inner], dtype `dtype`.
+ *   dout  : [batch, L, d_model], dtype `dtype`.
+ *   dy    : [batch, d_inner, L], dtype `dtype`, output, nullable (not computed).
+ *   dW    : [d_model, d_inner], dtype `dtype`, output, nullable (not computed);
+ *           at least one of dy and dW must be given.  dW is summed in a fixed
+ *           order, so repeated calls give identical bits.
+ * When the d_model x d_inner tiles of dW alone would leave the GPU idle,
+ * the sum over batch rows is split over several workgroups whose float32
+ * partials sit in a workspace the call allocates and frees stream-ordered
+ * (hipMallocAsync / hipFreeAsync; SSM_ENOMEM if that fails).
+ * Sizes: as ssm_out_proj, and W in float32 under 2^31 bytes.  Outputs must
+ * not overlap the inputs or each other.
+ * Errors: SSM_EINVAL, SSM_EUNSUPPORTED, SSM_ENOMEM, SSM_EHIP.
+ */
+int ssm_out_proj_bwd(const void *y, const void *W, const void *dout, void *dy, void *dW, int64_t batch,
+                     int64_t d_inner, int64_t d_model, int64_t L, int dtype, void *stream);
+
+/*
  * affine_scan -- inclusive scan of affine pairs along each row
  * ([Scan page] §1.2 and §2.1; [Mamba-2 page] §2.2).
  * A pair (a, b) is the map h -> a*h + b; composition, later step first, is

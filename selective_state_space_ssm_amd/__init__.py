@@ -17,8 +17,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["SSMError", "ssm_scan_fwd", "ssm_scan_fwd_states", "ssm_scan_fwd_conv", "ssm_scan_bwd",
-           "ssm_scan_bwd_conv", "ssm_step", "ssm_step_conv", "ssm_out_proj", "affine_scan", "affine_scan_order",
-           "plan_for", "library_path", "load_library", "PLANS"]
+           "ssm_scan_bwd_conv", "ssm_step", "ssm_step_conv", "ssm_out_proj", "ssm_out_proj_bwd", "affine_scan",
+           "affine_scan_order", "plan_for", "library_path", "load_library", "PLANS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmscan.so")
@@ -78,6 +78,8 @@ def load_library():
     lib.ssm_scan_plan_for.restype = I
     lib.ssm_out_proj.argtypes = [P, P, P, I64, I64, I64, I64, I, P]
     lib.ssm_out_proj.restype = I
+    lib.ssm_out_proj_bwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, P]
+    lib.ssm_out_proj_bwd.restype = I
     lib.affine_scan.argtypes = [P, P, P, P, I64, I64, P]
     lib.affine_scan.restype = I
     lib.affine_scan_order.argtypes = [ctypes.POINTER(I)] * 4
@@ -538,6 +540,36 @@ def ssm_out_proj(y: torch.Tensor, W: torch.Tensor, out: Optional[torch.Tensor] =
                               SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
     _check(rc)
     return out
+
+
+def ssm_out_proj_bwd(y: torch.Tensor, W: torch.Tensor, dout: torch.Tensor, want_dy: bool = True,
+                     want_dW: bool = True) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Gradients of ssm_out_proj (see ``ssm_out_proj_bwd`` in
+    include/ssm_scan.h) for dout [b, L, d_model]: returns (dy [b, d_inner, L]
+    or None, dW [d_model, d_inner] or None), in the dtype of y."""
+    device = y.device
+    if device.type != "cuda":
+        raise ValueError("ssm_out_proj_bwd needs CUDA/HIP tensors")
+    if y.dim() != 3 or W.dim() != 2 or dout.dim() != 3:
+        raise ValueError("y must be [b, d_inner, L], W [d_model, d_inner] and dout [b, L, d_model]")
+    if not (want_dy or want_dW):
+        raise ValueError("ask for dy, dW or both")
+    bsz, dk, L = y.shape
+    dm = W.shape[0]
+    dt = y.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    _need(y, "y", dt, device, (bsz, dk, L))
+    _need(W, "W", dt, device, (dm, dk))
+    _need(dout, "dout", dt, device, (bsz, L, dm))
+    dy = torch.empty_like(y) if want_dy else None
+    dW = torch.empty_like(W) if want_dW else None
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_out_proj_bwd(_ptr(y), _ptr(W), _ptr(dout), _ptr(dy), _ptr(dW), bsz, dk, dm, L,
+                                  SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
+    _check(rc)
+    return dy, dW
 
 
 def affine_scan(a: torch.Tensor, b: torch.Tensor, return_a: bool = True,

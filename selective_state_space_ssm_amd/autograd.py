@@ -6,6 +6,7 @@ marshalling only; every step runs in the library's kernels.
     y, last_state = selective_scan(u, delta, A, B, C, D, z, delta_bias,
                                    delta_softplus=True, h0=None, state_chunk=128)
     y, last_state = selective_scan_conv(x, conv_w, conv_b, delta, A, B, C, D, z, ...)
+    out = out_proj(y, W)          # the Linear after the gate, [b, L, d_model]
 
 Gradients flow to every tensor argument that requires them (dB and dC are
 computed in float32 and returned in the dtype of B and C).
@@ -16,9 +17,10 @@ from typing import Optional
 
 import torch
 
-from . import ssm_scan_bwd, ssm_scan_bwd_conv, ssm_scan_fwd_conv, ssm_scan_fwd_states
+from . import (ssm_out_proj, ssm_out_proj_bwd, ssm_scan_bwd, ssm_scan_bwd_conv, ssm_scan_fwd_conv,
+               ssm_scan_fwd_states)
 
-__all__ = ["selective_scan", "selective_scan_conv"]
+__all__ = ["selective_scan", "selective_scan_conv", "out_proj"]
 
 
 def _grad_or_zero(g, like):
@@ -84,3 +86,24 @@ def selective_scan_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[
     (u = silu(conv1d(x))): returns (y, last_state)."""
     return _SelectiveScanConv.apply(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, h0, delta_softplus,
                                     state_chunk)
+
+
+class _OutProj(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, y, W):
+        ctx.save_for_backward(y, W)
+        return ssm_out_proj(y, W)
+
+    @staticmethod
+    def backward(ctx, dout):
+        y, W = ctx.saved_tensors
+        dy, dW = ssm_out_proj_bwd(y, W, dout.contiguous(), want_dy=ctx.needs_input_grad[0],
+                                  want_dW=ctx.needs_input_grad[1])
+        return dy, dW
+
+
+def out_proj(y: torch.Tensor, W: torch.Tensor) -> torch.Tensor:
+    """Differentiable output projection: out[b, t, m] = sum_k W[m, k] y[b, k, t]
+    (y [b, d_inner, L] as the scan writes it, W [d_model, d_inner]); returns
+    [b, L, d_model]."""
+    return _OutProj.apply(y, W)

@@ -514,6 +514,50 @@ int ssm_out_proj(const void* y, const void* W, void* out, int64_t batch, int64_t
   return SSM_OK;
 }
 
+int ssm_out_proj_bwd(const void* y, const void* W, const void* dout, void* dy, void* dW, int64_t batch,
+                     int64_t d_inner, int64_t d_model, int64_t L, int dtype, void* stream) {
+  g_err.clear();
+  if (!y || !W || !dout) return fail(SSM_EINVAL, "y, W and dout must not be NULL");
+  if (!dy && !dW) return fail(SSM_EINVAL, "at least one of dy and dW must be given");
+  if (batch <= 0 || d_inner <= 0 || d_model <= 0 || L <= 0)
+    return fail(SSM_EINVAL, "sizes must be positive (batch=%lld d_inner=%lld d_model=%lld L=%lld)",
+                (long long)batch, (long long)d_inner, (long long)d_model, (long long)L);
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
+  const void* ptrs[] = {y, W, dout, dy, dW};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(SSM_EINVAL, "every pointer must be 16-byte aligned");
+  const int64_t es = dtype == SSM_F32 ? 4 : 2;
+  const int64_t lim = int64_t(1) << 31;
+  int64_t yrow, wsz, orow, w4, tmp;
+  if (!mul_ok(d_inner, L, &tmp) || !mul_ok(tmp, es, &yrow) || yrow >= lim || !mul_ok(d_model, d_inner, &tmp) ||
+      !mul_ok(tmp, es, &wsz) || !mul_ok(tmp, 4, &w4) || w4 >= lim || !mul_ok(L, d_model, &tmp) ||
+      !mul_ok(tmp, es, &orow) || orow >= lim)
+    return fail(SSM_EUNSUPPORTED, "a batch row of y or dout, or W in float32, reaches 2^31 bytes");
+  int64_t ybytes, obytes;
+  if (!mul_ok(yrow, batch, &ybytes) || !mul_ok(orow, batch, &obytes)) return fail(SSM_EINVAL, "tensor sizes overflow");
+  ssm::ProjBwdArgs a{y, W, dout, dy, dW, batch, d_inner, d_model, L};
+  const bool bf16 = dtype == SSM_BF16;
+  if (ssm::proj_bwd_tiles(bf16, a) >= lim) return fail(SSM_EUNSUPPORTED, "too many output tiles for one launch");
+  const Range ins[] = {range_of(y, uint64_t(ybytes)), range_of(W, uint64_t(wsz)), range_of(dout, uint64_t(obytes))};
+  const Range rdy = range_of(dy, uint64_t(ybytes)), rdw = range_of(dW, uint64_t(wsz));
+  for (const Range& r : ins)
+    if (overlap(rdy, r) || overlap(rdw, r)) return fail(SSM_EINVAL, "dy and dW must not overlap y, W or dout");
+  if (overlap(rdy, rdw)) return fail(SSM_EINVAL, "dy and dW overlap");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t wbytes = ssm::proj_bwd_workspace_bytes(bf16, a);
+  void* ws = nullptr;
+  if (wbytes > 0) {
+    hipError_t e = hipMallocAsync(&ws, wbytes, st);
+    if (e == hipErrorOutOfMemory) return fail(SSM_ENOMEM, "dW split workspace of %zu bytes", wbytes);
+    if (e != hipSuccess) return hip_fail(e, "dW split workspace allocation");
+  }
+  hipError_t e = ssm::launch_out_proj_bwd(a, bf16, static_cast<float*>(ws), wbytes, st);
+  hipError_t ef = ws ? hipFreeAsync(ws, st) : hipSuccess;
+  if (e != hipSuccess) return hip_fail(e, "out-projection backward launch");
+  if (ef != hipSuccess) return hip_fail(ef, "dW split workspace release");
+  return SSM_OK;
+}
+
 int affine_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t rows, int64_t L,
                 void* stream) {
   g_err.clear();

@@ -141,4 +141,21 @@ hipError_t launch_out_proj(const ProjArgs& a, bool bf16, hipStream_t st);
 // workgroups of one launch
 int64_t proj_tiles(bool bf16, int64_t batch, int64_t d_model, int64_t L);
 
+// Gradients of the output projection for dout [batch][L][d_model]:
+// dy[b][k][t] = sum_m W[m][k] dout[b][t][m], dW[m][k] = sum_{b,t}
+// dout[b][t][m] y[b][k][t].  dy or dw may be null (not computed).  dW may
+// split its sum over the batch rows into float32 partials in `work`
+// (proj_bwd_workspace_bytes; the split is skipped when work is null).
+struct ProjBwdArgs {
+  const void* y;      // [batch][d_inner][L]
+  const void* w;      // [d_model][d_inner]
+  const void* dout;   // [batch][L][d_model]
+  void* dy;           // [batch][d_inner][L], nullable
+  void* dw;           // [d_model][d_inner], nullable
+  int64_t batch, d_inner, d_model, L;
+};
+size_t proj_bwd_workspace_bytes(bool bf16, const ProjBwdArgs& a);
+int64_t proj_bwd_tiles(bool bf16, const ProjBwdArgs& a);
+hipError_t launch_out_proj_bwd(const ProjBwdArgs& a, bool bf16, float* work, size_t work_bytes, hipStream_t st);
+
 }  // namespace ssm

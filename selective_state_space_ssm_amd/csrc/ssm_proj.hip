@@ -1,26 +1,42 @@
-// Output projection after the gated scan, on the matrix cores of gfx950:
+// Output projection after the gated scan, and its gradients, on the matrix
+// cores of gfx950:
 //
-//   out[b, t, m] = sum_k W[m, k] * y[b, k, t]
+//   out[b, t, m] = sum_k W[m, k] * y[b, k, t]                     (forward)
+//   dy[b, k, t]  = sum_m W[m, k] * dout[b, t, m]                  (grad of y)
+//   dW[m, k]     = sum_{b, t} dout[b, t, m] * y[b, k, t]          (grad of W)
 //
 // ([Mamba-2 page] §4.1 lists this Linear last in the fused chain: Conv1D,
-// SSM, SiLU gate, Linear.)  Unlike the scan it is a dense contraction over
-// d_inner, so it runs as MFMA tiles with float32 accumulation.
+// SSM, SiLU gate, Linear.)  Unlike the scan these are dense contractions, so
+// they run as MFMA tiles with float32 accumulation.
 //
-// Layout.  y is [b][d_inner][L] as the scan writes it (L contiguous), W is
-// [d_model][d_inner] (d_inner contiguous), out is [b][L][d_model] (token
-// major, the layout of the residual stream).  y is read in place: no
-// transposed copy is made in HBM.
+// One kernel serves all three.  It computes C^T = A B, i.e.
+//
+//   out[n][m] = sum_k A[m][k] * B[k][n]
+//
+// with A row-major [M][K] (K contiguous), B row-major [K][N] (N contiguous)
+// and out row-major [N][M] (M contiguous), for `batch` independent outputs
+// (each operand with its own batch stride, 0 = shared) and, inside one
+// output, a sum over `nseg` segments of K (each operand with its own segment
+// stride).  With y [b][d_inner][L], W [d_model][d_inner], dout
+// [b][L][d_model]:
+//
+//   forward  A = W,       B = y[b],     M = d_model, N = L,       K = d_inner
+//   dy       A = dout[b], B = W,        M = L,       N = d_inner, K = d_model
+//   dW       A = y[b],    B = dout[b],  M = d_inner, N = d_model, K = L, the
+//            batch rows being the segments summed
+//
+// so every operand is read in place, in the layout the rest of the block
+// keeps it in.
 //
 // Tiling.  A workgroup of 256 threads (4 wavefronts in a 2 x 2 grid) owns a
-// BM (d_model) x BN (token) tile of one batch row and walks d_inner in steps
-// of BK values (128 bytes: 64 bfloat16 or 32 float32).  Each step stages the
-// W slice [BM][BK] and the y slice [BK][BN] into LDS, the y slice transposed
-// to [token][k] on the way in (an E x E register transpose per thread, E =
-// values per 16 bytes), so that both MFMA operands read E consecutive k of
-// one row with one 128-bit LDS read.  Each wavefront owns (BM/2) x (BN/2):
-// a TI x TJ grid of 16 x 16 MFMA tiles.  Two LDS buffers: the next step's
-// global loads are issued before this step's MFMAs and written to the other
-// buffer after them, with one barrier per step.
+// BM (M) x BN (N) tile and walks K in steps of BK values (128 bytes: 64
+// bfloat16 or 32 float32).  Each step stages the A slice [BM][BK] and the B
+// slice [BK][BN] into LDS, B transposed to [n][k] on the way in (an E x E
+// register transpose per thread, E = values per 16 bytes), so that both MFMA
+// operands read E consecutive k of one row with one 128-bit LDS read.  Each
+// wavefront owns (BM/2) x (BN/2): a TI x TJ grid of 16 x 16 MFMA tiles.  Two
+// LDS buffers: the next step's global loads are issued before this step's
+// MFMAs and written to the other buffer after them, one barrier per step.
 //
 //   bfloat16: v_mfma_f32_16x16x32_bf16, BM = BN = 256 (TI = TJ = 8, 256
 //             accumulators per lane, one workgroup per CU, 128 KB of LDS)
@@ -28,20 +44,26 @@
 //             order inside a 16-value step permuted identically for both
 //             operands so that each lane reads 4 consecutive k at once
 //
+// When the output tiles alone would leave CUs idle (dW: d_model x d_inner
+// tiles only), the segments are split over `nsplit` workgroups per tile;
+// each writes a float32 partial and a second kernel sums the partials in a
+// fixed order (the result is the same from run to run).
+//
 // LDS rows are 128 bytes (8 chunks of 16 bytes) without padding; chunk c of
 // row r sits at position c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7.  The MFMA
-// operand reads (16 consecutive rows, one chunk) and the transposing y writes
-// (rows E apart, one chunk) then both spread every 8 lanes over the 8 chunk
-// positions, i.e. over all banks.
+// operand reads (16 consecutive rows, one chunk) and the transposing B
+// writes (rows E apart, one chunk) then both spread every 8 lanes over the 8
+// chunk positions.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile order is
-// remapped so that each XCD takes a contiguous range of tiles, d_model tiles
-// fastest: the workgroups that share a y slice share one L2.
+// remapped so that each XCD takes a contiguous range of tiles, M tiles
+// fastest: the workgroups that share a B slice share one L2.
 //
-// Bounds.  Global accesses go through buffer resources (one per batch row
-// for y and out): an out-of-range offset reads zero and drops a write.  Rows
-// or columns past the edge of the problem get such an offset, so partial
-// tiles load zeros (contributing nothing to the sums) and store nothing.
+// Bounds.  Global accesses go through buffer resources (one per operand,
+// batch and segment): an out-of-range offset reads zero and drops a write.
+// Rows or columns past the edge of the problem get such an offset, so
+// partial tiles load zeros (contributing nothing to the sums) and store
+// nothing.
 //
 // Pages cited:
 //   [Mamba-2 page] "Mamba (part 2): parallel scan and hardware-aware
@@ -60,7 +82,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPThreads = 256;
-constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource (sizes are < 2^31)
+constexpr uint32_t kOOB = 0x80000000u;    // an offset past every resource (sizes are < 2^31)
+constexpr int64_t kFillWorkgroups = 512;  // split the segments until about this many workgroups
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -69,8 +92,8 @@ struct ProjCfg;
 template <>
 struct ProjCfg<F32> {
   static constexpr int E = 4;     // values per 16-byte chunk
-  static constexpr int TI = 4;    // 16 x 16 tiles per wavefront along d_model
-  static constexpr int TJ = 4;    // ... along tokens
+  static constexpr int TI = 4;    // 16 x 16 tiles per wavefront along M
+  static constexpr int TJ = 4;    // ... along N
   static constexpr int ES = 4;    // bytes per value
 };
 template <>
@@ -81,11 +104,18 @@ struct ProjCfg<BF16> {
   static constexpr int ES = 2;
 };
 
-struct ProjDev {
-  const char* y;
-  const char* w;
-  char* out;
-  int64_t batch, K, M, L;   // K = d_inner, M = d_model
+// One launch: out[bt][n][m] = sum over segments s and k of
+// A[bt][s][m][k] * B[bt][s][k][n].  Strides in elements.
+struct GemmDev {
+  const char* a;
+  const char* b;
+  char* out;        // IO-typed output, or (PART) float32 partials [batch][nsplit][N][M]
+  int64_t M, N, K;
+  int64_t lda, ldb, ldo;
+  int64_t a_batch, b_batch, o_batch;
+  int64_t a_seg, b_seg;
+  int64_t nseg, spp;    // segments, segments per split
+  int64_t nsplit, batch;
 };
 
 template <typename IO>
@@ -98,132 +128,147 @@ constexpr size_t proj_lds_bytes() { return size_t(2) * (proj_bm<IO>() + proj_bn<
 // 8 bfloat16 values -> MFMA operand
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <typename IO, bool VEC>
-__global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
+template <typename IO, bool VEC, bool PART>
+__global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) {
   using C = ProjCfg<IO>;
   constexpr int E = C::E, TI = C::TI, TJ = C::TJ, ES = C::ES;
   constexpr int BM = proj_bm<IO>(), BN = proj_bn<IO>(), BK = 8 * E;
-  constexpr int NW = BM / 32;                   // W chunks per thread per step
-  static_assert(BN / E == 32, "one E x E block of y per thread per step");
+  constexpr int NW = BM / 32;                   // A chunks per thread per step
+  static_assert(BN / E == 32, "one E x E block of B per thread per step");
 
   extern __shared__ uint4 lds[];                // [2][BM + BN][8] chunks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- tile of this workgroup (XCD-contiguous order, d_model tiles fastest)
-  const int64_t nm = (p.M + BM - 1) / BM, nl = (p.L + BN - 1) / BN;
+  // ---- tile of this workgroup (XCD-contiguous order, M tiles fastest)
+  const int64_t nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
   const int64_t G = static_cast<int64_t>(gridDim.x);
   const int64_t pid = blockIdx.x, q = G / 8, r = G % 8, xcd = pid % 8, slot = pid / 8;
   const int64_t logical = xcd * q + (xcd < r ? xcd : r) + slot;
-  const int64_t mt = logical % nm, rest = logical / nm;
-  const int64_t lt = rest % nl, b = rest / nl;
-  const int64_t m0 = mt * BM, l0 = lt * BN;
-
-  const uint32_t ybytes = static_cast<uint32_t>(p.K * p.L * ES);
-  const Rsrc ry = make_rsrc(p.y + b * p.K * p.L * ES, ybytes);
-  const Rsrc rw = make_rsrc(p.w, static_cast<uint32_t>(p.M * p.K * ES));
-  const Rsrc ro = make_rsrc(p.out + b * p.L * p.M * ES, static_cast<uint32_t>(p.L * p.M * ES));
+  const int64_t mt = logical % nm;
+  int64_t rest = logical / nm;
+  const int64_t nt = rest % nn;
+  rest /= nn;
+  const int64_t split = rest % p.nsplit, bt = rest / p.nsplit;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t seg0 = split * p.spp;
+  const int64_t seg1 = (seg0 + p.spp < p.nseg) ? seg0 + p.spp : p.nseg;
 
   // ---- per-thread load roles
-  // W: chunk c of rows (tid >> 3) + 32 i;  y: k-group kg (E rows), token group tg (E tokens)
+  // A: chunk c of rows (tid >> 3) + 32 i;  B: k-group kg (E rows), n group tg (E columns)
   const int wc = tid & 7, wr0 = tid >> 3;
   const int tg = tid & 31, kg = tid >> 5;
-  const int64_t ytok = l0 + tg * E;
+  const int64_t bcol = n0 + tg * E;
 
-  uint4 wreg[NW];
-  uint4 yreg[E];
+  uint4 areg[NW];
+  uint4 breg[E];
 
   // 32-bit byte offsets: a per-thread base plus uniform steps.  Every valid
   // offset is below 2^31; invalid ones are replaced by kOOB before use.
-  const uint32_t wstride = static_cast<uint32_t>(p.K * ES);          // bytes per W row
-  const uint32_t ystride = static_cast<uint32_t>(p.L * ES);          // bytes per y row
-  const int64_t wm0 = m0 + wr0;
-  const uint32_t wbase = static_cast<uint32_t>(wm0 * wstride + wc * E * ES);
-  const uint32_t ybase = static_cast<uint32_t>(kg * E * static_cast<int64_t>(ystride) + ytok * ES);
-  const int wrows_ok = wm0 >= p.M ? 0 : static_cast<int>((p.M - wm0 + 31) / 32);   // valid i < this
+  const uint32_t astride = static_cast<uint32_t>(p.lda * ES);        // bytes per A row
+  const uint32_t bstride = static_cast<uint32_t>(p.ldb * ES);        // bytes per B row
+  const int64_t am0 = m0 + wr0;
+  const uint32_t abase = static_cast<uint32_t>(am0 * astride + wc * E * ES);
+  const uint32_t bbase = static_cast<uint32_t>(kg * E * static_cast<int64_t>(bstride) + bcol * ES);
+  const int arows_ok = am0 >= p.M ? 0 : static_cast<int>((p.M - am0 + 31) / 32);   // valid i < this
+  const bool bcol_ok = bcol < p.N;
+  const uint32_t abytes = static_cast<uint32_t>(p.M * p.lda * ES);
+  const uint32_t bbytes = static_cast<uint32_t>(p.K * p.ldb * ES);
 
-  auto load_w_chunk = [&](int i, int64_t k0) -> uint4 {
-    const int64_t k = k0 + wc * E;
-    const uint32_t off = wbase + static_cast<uint32_t>(i * 32) * wstride + static_cast<uint32_t>(k0 * ES);
-    if constexpr (VEC) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, (i < wrows_ok && k < p.K) ? off : kOOB, 0, 0);
-      return make_uint4(v.x, v.y, v.z, v.w);
-    } else {
-      uint32_t w[4] = {0, 0, 0, 0};
+  auto krem_of = [&](int64_t k0) -> int {   // values of K left from k0, clamped to [-1, BK]
+    const int64_t rr = p.K - k0;
+    return rr < 0 ? -1 : (rr > BK ? BK : static_cast<int>(rr));
+  };
+  // step s of this workgroup: segment seg0 + s / ksteps, k0 = (s % ksteps) * BK
+  const int64_t ksteps = (p.K + BK - 1) / BK;
+  const int64_t nsteps = (seg1 - seg0) * ksteps;
+  auto load_global = [&](int64_t s) {
+    const int64_t seg = seg0 + s / ksteps;
+    const int64_t k0 = (s % ksteps) * BK;
+    const Rsrc ra = make_rsrc(p.a + (bt * p.a_batch + seg * p.a_seg) * ES, abytes);
+    const Rsrc rb = make_rsrc(p.b + (bt * p.b_batch + seg * p.b_seg) * ES, bbytes);
+    const int krem = krem_of(k0);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint32_t oe = (i < wrows_ok && k + e < p.K) ? off + e * ES : kOOB;
-        if constexpr (ES == 4) {
-          w[e] = __builtin_amdgcn_raw_buffer_load_b32(rw, oe, 0, 0);
-        } else {
-          const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rw, oe, 0, 0);
-          w[e >> 1] |= (e & 1) ? (h << 16) : h;
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t off = abase + static_cast<uint32_t>(i * 32) * astride + static_cast<uint32_t>(k0 * ES);
+      if constexpr (VEC) {
+        const bool ok = (i < arows_ok) & (wc * E < krem);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? off : kOOB, 0, 0);
+        areg[i] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool ok = (i < arows_ok) & (wc * E + e < krem);
+          const uint32_t oe = ok ? off + e * ES : kOOB;
+          if constexpr (ES == 4) {
+            w[e] = __builtin_amdgcn_raw_buffer_load_b32(ra, oe, 0, 0);
+          } else {
+            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(ra, oe, 0, 0);
+            w[e >> 1] |= (e & 1) ? (h << 16) : h;
+          }
         }
+        areg[i] = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < E; ++rr) {
+      const uint32_t off = bbase + static_cast<uint32_t>(rr) * bstride + static_cast<uint32_t>(k0 * p.ldb * ES);
+      if constexpr (VEC) {
+        const bool ok = (kg * E + rr < krem) & bcol_ok;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? off : kOOB, 0, 0);
+        breg[rr] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool ok = (kg * E + rr < krem) & (bcol + e < p.N);
+          const uint32_t oe = ok ? off + e * ES : kOOB;
+          if constexpr (ES == 4) {
+            w[e] = __builtin_amdgcn_raw_buffer_load_b32(rb, oe, 0, 0);
+          } else {
+            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rb, oe, 0, 0);
+            w[e >> 1] |= (e & 1) ? (h << 16) : h;
+          }
+        }
+        breg[rr] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   };
-  auto load_y_row = [&](int rr, int64_t k0) -> uint4 {
-    const int64_t k = k0 + kg * E + rr;
-    const uint32_t off = ybase + static_cast<uint32_t>(rr) * ystride + static_cast<uint32_t>(k0 * ystride);
-    if constexpr (VEC) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ry, (k < p.K && ytok < p.L) ? off : kOOB, 0, 0);
-      return make_uint4(v.x, v.y, v.z, v.w);
-    } else {
-      uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint32_t oe = (k < p.K && ytok + e < p.L) ? off + e * ES : kOOB;
-        if constexpr (ES == 4) {
-          w[e] = __builtin_amdgcn_raw_buffer_load_b32(ry, oe, 0, 0);
-        } else {
-          const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(ry, oe, 0, 0);
-          w[e >> 1] |= (e & 1) ? (h << 16) : h;
-        }
-      }
-      return make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  };
-  auto load_global = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < NW; ++i) wreg[i] = load_w_chunk(i, k0);
-#pragma unroll
-    for (int rr = 0; rr < E; ++rr) yreg[rr] = load_y_row(rr, k0);
-  };
-  // registers -> LDS buffer `buf`: W rows as they are, y as [token][k]
+  // registers -> LDS buffer `buf`: A rows as they are, B as [n][k]
   auto store_lds = [&](int buf) {
-    uint4* sw = lds + buf * (BM + BN) * 8;
-    uint4* sy = sw + BM * 8;
+    uint4* sa = lds + buf * (BM + BN) * 8;
+    uint4* sb = sa + BM * 8;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int row = wr0 + 32 * i;
-      sw[row * 8 + (wc ^ swz(row))] = wreg[i];
+      sa[row * 8 + (wc ^ swz(row))] = areg[i];
     }
     if constexpr (ES == 2) {
-      // 8 k-rows of 8 tokens -> 8 tokens of 8 k (k pairs packed low, high)
+      // 8 k-rows of 8 columns -> 8 columns of 8 k (k pairs packed low, high)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int pw = j >> 1;
         uint32_t o[4];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const uint32_t lo = reinterpret_cast<const uint32_t*>(&yreg[2 * qd])[pw];
-          const uint32_t hi = reinterpret_cast<const uint32_t*>(&yreg[2 * qd + 1])[pw];
+          const uint32_t lo = reinterpret_cast<const uint32_t*>(&breg[2 * qd])[pw];
+          const uint32_t hi = reinterpret_cast<const uint32_t*>(&breg[2 * qd + 1])[pw];
           o[qd] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
         }
         const int row = tg * 8 + j;
-        sy[row * 8 + (kg ^ swz(row))] = make_uint4(o[0], o[1], o[2], o[3]);
+        sb[row * 8 + (kg ^ swz(row))] = make_uint4(o[0], o[1], o[2], o[3]);
       }
     } else {
-      // 4 k-rows of 4 tokens -> 4 tokens of 4 k
+      // 4 k-rows of 4 columns -> 4 columns of 4 k
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = tg * 4 + j;
-        const uint4 v = make_uint4(reinterpret_cast<const uint32_t*>(&yreg[0])[j],
-                                   reinterpret_cast<const uint32_t*>(&yreg[1])[j],
-                                   reinterpret_cast<const uint32_t*>(&yreg[2])[j],
-                                   reinterpret_cast<const uint32_t*>(&yreg[3])[j]);
-        sy[row * 8 + (kg ^ swz(row))] = v;
+        const uint4 v = make_uint4(reinterpret_cast<const uint32_t*>(&breg[0])[j],
+                                   reinterpret_cast<const uint32_t*>(&breg[1])[j],
+                                   reinterpret_cast<const uint32_t*>(&breg[2])[j],
+                                   reinterpret_cast<const uint32_t*>(&breg[3])[j]);
+        sb[row * 8 + (kg ^ swz(row))] = v;
       }
     }
   };
@@ -249,17 +294,17 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
   // both k-steps' fragments are read first (the reads overlap each other and
   // the first MFMAs wait only for their own operands), then 2 x TI x TJ MFMAs
   auto compute = [&](int buf) {
-    const char* abase = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + wm * (BM / 2) * 128;
-    const char* bbase = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + BM * 128 + wn * (BN / 2) * 128;
+    const char* fa_base = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + wm * (BM / 2) * 128;
+    const char* fb_base = reinterpret_cast<const char*>(lds + buf * (BM + BN) * 8) + BM * 128 + wn * (BN / 2) * 128;
     uint4 fa[2][TI], fb[2][TJ];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        fa[s][i] = *reinterpret_cast<const uint4*>(abase + loff[((4 * s) ^ (2 * (i & 3))) >> 1] + 2048 * i);
+        fa[s][i] = *reinterpret_cast<const uint4*>(fa_base + loff[((4 * s) ^ (2 * (i & 3))) >> 1] + 2048 * i);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        fb[s][j] = *reinterpret_cast<const uint4*>(bbase + loff[((4 * s) ^ (2 * (j & 3))) >> 1] + 2048 * j);
+        fb[s][j] = *reinterpret_cast<const uint4*>(fb_base + loff[((4 * s) ^ (2 * (j & 3))) >> 1] + 2048 * j);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -287,28 +332,40 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
     }
   };
 
-  const int64_t nk = (p.K + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
+  if (nsteps > 0) {
+    load_global(0);
+    store_lds(0);
+  }
   __syncthreads();
-  for (int64_t it = 0; it < nk; ++it) {
-    const bool more = it + 1 < nk;
-    if (more) load_global((it + 1) * BK);
-    compute(static_cast<int>(it & 1));
-    if (more) store_lds(static_cast<int>((it + 1) & 1));
+  for (int64_t s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) load_global(s + 1);
+    compute(static_cast<int>(s & 1));
+    if (more) store_lds(static_cast<int>((s + 1) & 1));
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds d_model rows 4*lgrp + v of column (lane & 15)
+  // ---- epilogue: lane holds rows 4*lgrp + v (M) of column (lane & 15) (N)
+  const Rsrc ro = PART ? make_rsrc(p.out + ((bt * p.nsplit + split) * p.N * p.M) * 4,
+                                   static_cast<uint32_t>(p.N * p.M * 4))
+                       : make_rsrc(p.out + bt * p.o_batch * ES, static_cast<uint32_t>(p.N * p.ldo * ES));
+  const int64_t ldo = PART ? p.M : p.ldo;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * lgrp;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int64_t t = l0 + wn * (BN / 2) + 16 * j + (lane & 15);
+      const int64_t n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
       const f32x4 v = acc[i][j];
-      if constexpr (VEC) {
-        const uint32_t off = (t < p.L && m < p.M) ? static_cast<uint32_t>(t * p.M + m) * ES : kOOB;
+      if constexpr (PART) {
+        // float32 partial, dense [N][M]; M % 4 == 0 on this path
+        const uint32_t off = (n < p.N && m < p.M) ? static_cast<uint32_t>(n * ldo + m) * 4 : kOOB;
+        u32x4 w;
+        w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
+        w.z = __float_as_uint(v[2]); w.w = __float_as_uint(v[3]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
+      } else if constexpr (VEC) {
+        const uint32_t off = (n < p.N && m < p.M) ? static_cast<uint32_t>(n * ldo + m) * ES : kOOB;
         if constexpr (ES == 4) {
           u32x4 w;
           w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
@@ -323,7 +380,7 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t off = (t < p.L && m + e < p.M) ? static_cast<uint32_t>(t * p.M + m + e) * ES : kOOB;
+          const uint32_t off = (n < p.N && m + e < p.M) ? static_cast<uint32_t>(n * ldo + m + e) * ES : kOOB;
           if constexpr (ES == 4)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), ro, off, 0, 0);
           else
@@ -334,19 +391,132 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_out_proj_kernel(ProjDev p) {
   }
 }
 
-template <typename IO, bool VEC>
-hipError_t launch_proj_t(const ProjArgs& h, hipStream_t st) {
+// out[bt][n][m] = sum_{s < nsplit} part[bt][s][n][m], summed in split order;
+// four consecutive m per thread (M % 4 == 0 on the split path).
+template <typename IO>
+__global__ void __launch_bounds__(256) ssm_proj_reduce_kernel(const float* __restrict__ part, char* out, int64_t N,
+                                                              int64_t M, int64_t ldo, int64_t o_batch,
+                                                              int64_t nsplit, int64_t batch) {
+  using T = typename IO::T;
+  const int64_t per = N * M / 4;
+  const int64_t total = per * batch;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t bt = i / per, e4 = (i % per) * 4;
+    const int64_t n = e4 / M, m = e4 % M;
+    const float4* src = reinterpret_cast<const float4*>(part + bt * nsplit * N * M + e4);
+    float4 s = src[0];
+    for (int64_t k = 1; k < nsplit; ++k) {
+      const float4 v = src[k * per];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const float o[4] = {s.x, s.y, s.z, s.w};
+    IO::template st<4>(reinterpret_cast<T*>(out) + bt * o_batch + n * ldo + m, o);
+  }
+}
+
+template <typename IO, bool VEC, bool PART>
+hipError_t launch_gemm_t(const GemmDev& p, hipStream_t st) {
   constexpr int BM = proj_bm<IO>(), BN = proj_bn<IO>();
-  ProjDev p{static_cast<const char*>(h.y), static_cast<const char*>(h.w), static_cast<char*>(h.out), h.batch,
-            h.d_inner, h.d_model, h.L};
-  const int64_t tiles = ((h.d_model + BM - 1) / BM) * ((h.L + BN - 1) / BN) * h.batch;
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.nsplit * p.batch;
   const size_t smem = proj_lds_bytes<IO>();
-  auto kern = ssm_out_proj_kernel<IO, VEC>;
+  auto kern = ssm_proj_gemm_kernel<IO, VEC, PART>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), smem, st, p);
   return hipGetLastError();
+}
+
+template <typename IO>
+int64_t tiles_of(const GemmDev& p) {
+  return ((p.M + proj_bm<IO>() - 1) / proj_bm<IO>()) * ((p.N + proj_bn<IO>() - 1) / proj_bn<IO>()) * p.batch;
+}
+
+// Segments per split for a contraction: more than one workgroup per tile
+// only when the segments can be split, the tiles alone leave the chip idle,
+// and M allows the float32 partials' vector stores.  Returns spp (= nseg:
+// no split).
+template <typename IO>
+int64_t split_spp(const GemmDev& p) {
+  if (p.nseg <= 1 || p.M % 4 != 0) return p.nseg;
+  const int64_t tiles = tiles_of<IO>(p);
+  int64_t want = (kFillWorkgroups + tiles - 1) / tiles;
+  if (want > p.nseg) want = p.nseg;
+  if (want <= 1) return p.nseg;
+  return (p.nseg + want - 1) / want;
+}
+
+template <typename IO>
+int64_t split_floats_of(const GemmDev& p) {
+  const int64_t spp = split_spp<IO>(p);
+  if (spp >= p.nseg) return 0;
+  return ((p.nseg + spp - 1) / spp) * p.batch * p.N * p.M;
+}
+
+// One contraction: split its segments over workgroups (float32 partials in
+// `work`, then the fixed-order sum) when that pays and the workspace is
+// there; else one workgroup per tile writes out directly.
+template <typename IO>
+hipError_t run_gemm(GemmDev p, float* work, int64_t work_floats, hipStream_t st) {
+  const int64_t E = ProjCfg<IO>::E;
+  const bool vec = p.K % E == 0 && p.N % E == 0 && p.M % 4 == 0;
+  const int64_t need = split_floats_of<IO>(p);
+  if (need == 0 || work == nullptr || need > work_floats) {
+    p.spp = p.nseg;
+    p.nsplit = 1;
+    return vec ? launch_gemm_t<IO, true, false>(p, st) : launch_gemm_t<IO, false, false>(p, st);
+  }
+  p.spp = split_spp<IO>(p);
+  p.nsplit = (p.nseg + p.spp - 1) / p.spp;
+  char* out = p.out;
+  p.out = reinterpret_cast<char*>(work);
+  hipError_t e = vec ? launch_gemm_t<IO, true, true>(p, st) : launch_gemm_t<IO, false, true>(p, st);
+  if (e != hipSuccess) return e;
+  const int64_t n4 = p.batch * p.N * p.M / 4;
+  const int64_t blocks = n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096;
+  hipLaunchKernelGGL(ssm_proj_reduce_kernel<IO>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     static_cast<const float*>(work), out, p.N, p.M, p.ldo, p.o_batch, p.nsplit, p.batch);
+  return hipGetLastError();
+}
+
+GemmDev forward_desc(const ProjArgs& h) {
+  GemmDev p{};
+  p.a = static_cast<const char*>(h.w);
+  p.b = static_cast<const char*>(h.y);
+  p.out = static_cast<char*>(h.out);
+  p.M = h.d_model; p.N = h.L; p.K = h.d_inner;
+  p.lda = h.d_inner; p.ldb = h.L; p.ldo = h.d_model;
+  p.a_batch = 0; p.b_batch = h.d_inner * h.L; p.o_batch = h.L * h.d_model;
+  p.a_seg = 0; p.b_seg = 0;
+  p.nseg = 1; p.spp = 1; p.nsplit = 1; p.batch = h.batch;
+  return p;
+}
+
+GemmDev dy_desc(const ProjBwdArgs& h) {
+  GemmDev p{};
+  p.a = static_cast<const char*>(h.dout);
+  p.b = static_cast<const char*>(h.w);
+  p.out = static_cast<char*>(h.dy);
+  p.M = h.L; p.N = h.d_inner; p.K = h.d_model;
+  p.lda = h.d_model; p.ldb = h.d_inner; p.ldo = h.L;
+  p.a_batch = h.L * h.d_model; p.b_batch = 0; p.o_batch = h.d_inner * h.L;
+  p.a_seg = 0; p.b_seg = 0;
+  p.nseg = 1; p.spp = 1; p.nsplit = 1; p.batch = h.batch;
+  return p;
+}
+
+GemmDev dw_desc(const ProjBwdArgs& h) {
+  GemmDev p{};
+  p.a = static_cast<const char*>(h.y);
+  p.b = static_cast<const char*>(h.dout);
+  p.out = static_cast<char*>(h.dw);
+  p.M = h.d_inner; p.N = h.d_model; p.K = h.L;
+  p.lda = h.L; p.ldb = h.d_model; p.ldo = h.d_inner;
+  p.a_batch = 0; p.b_batch = 0; p.o_batch = 0;
+  p.a_seg = h.d_inner * h.L; p.b_seg = h.L * h.d_model;
+  p.nseg = h.batch; p.spp = h.batch; p.nsplit = 1; p.batch = 1;
+  return p;
 }
 
 }  // namespace
@@ -357,11 +527,37 @@ int64_t proj_tiles(bool bf16, int64_t batch, int64_t d_model, int64_t L) {
   return ((d_model + bm - 1) / bm) * ((L + bn - 1) / bn) * batch;
 }
 
+int64_t proj_bwd_tiles(bool bf16, const ProjBwdArgs& h) {
+  const GemmDev a = dy_desc(h), b = dw_desc(h);
+  const int64_t ta = bf16 ? tiles_of<BF16>(a) : tiles_of<F32>(a);
+  const int64_t tb = (bf16 ? tiles_of<BF16>(b) : tiles_of<F32>(b)) * h.batch;
+  return ta > tb ? ta : tb;
+}
+
+size_t proj_bwd_workspace_bytes(bool bf16, const ProjBwdArgs& h) {
+  if (h.dw == nullptr) return 0;
+  const GemmDev p = dw_desc(h);
+  return sizeof(float) * static_cast<size_t>(bf16 ? split_floats_of<BF16>(p) : split_floats_of<F32>(p));
+}
+
 hipError_t launch_out_proj(const ProjArgs& h, bool bf16, hipStream_t st) {
-  const int64_t E = bf16 ? 8 : 4;
-  const bool vec = h.d_inner % E == 0 && h.L % E == 0 && h.d_model % 4 == 0;
-  if (bf16) return vec ? launch_proj_t<BF16, true>(h, st) : launch_proj_t<BF16, false>(h, st);
-  return vec ? launch_proj_t<F32, true>(h, st) : launch_proj_t<F32, false>(h, st);
+  const GemmDev p = forward_desc(h);
+  return bf16 ? run_gemm<BF16>(p, nullptr, 0, st) : run_gemm<F32>(p, nullptr, 0, st);
+}
+
+hipError_t launch_out_proj_bwd(const ProjBwdArgs& h, bool bf16, float* work, size_t work_bytes, hipStream_t st) {
+  const int64_t wf = static_cast<int64_t>(work_bytes / sizeof(float));
+  if (h.dy != nullptr) {
+    const GemmDev p = dy_desc(h);
+    const hipError_t e = bf16 ? run_gemm<BF16>(p, nullptr, 0, st) : run_gemm<F32>(p, nullptr, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  if (h.dw != nullptr) {
+    const GemmDev p = dw_desc(h);
+    const hipError_t e = bf16 ? run_gemm<BF16>(p, work, wf, st) : run_gemm<F32>(p, work, wf, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ssm

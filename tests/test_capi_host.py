@@ -247,3 +247,21 @@ def test_out_proj_rejects_bad_arguments():
     assert call(k=1 << 16, L=1 << 15) == ssm.SSM_EUNSUPPORTED          # a y row of 2^32 bytes
     assert call(m=1 << 20, k=1 << 11) == ssm.SSM_EUNSUPPORTED          # W of 2^32 bytes
     assert "2^31" in lib.ssm_last_error().decode()
+
+
+def test_out_proj_bwd_rejects_bad_arguments():
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    y, w, dout, dy, dw = P(BIG), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG)
+
+    def call(y=y, w=w, dout=dout, dy=dy, dw=dw, b=2, k=64, m=32, L=128, dtype=ssm.SSM_BF16):
+        return lib.ssm_out_proj_bwd(y, w, dout, dy, dw, b, k, m, L, dtype, None)
+
+    assert call(dout=None) == ssm.SSM_EINVAL
+    assert call(dy=None, dw=None) == ssm.SSM_EINVAL                    # nothing asked for
+    assert call(m=0) == ssm.SSM_EINVAL
+    assert call(dtype=5) == ssm.SSM_EUNSUPPORTED
+    assert call(dy=P(4 * BIG + 4)) == ssm.SSM_EINVAL                   # misaligned
+    assert call(dw=P(BIG + 256)) == ssm.SSM_EINVAL                     # dW inside y
+    assert call(dw=P(4 * BIG + 64)) == ssm.SSM_EINVAL                  # dW inside dy
+    assert call(m=1 << 16, k=1 << 14) == ssm.SSM_EUNSUPPORTED          # W in float32 reaches 2^32 bytes

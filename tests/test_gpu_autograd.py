@@ -15,7 +15,7 @@ import torch
 
 import workloads
 from oracle import ref
-from selective_state_space_ssm_amd.autograd import selective_scan, selective_scan_conv
+from selective_state_space_ssm_amd.autograd import out_proj, selective_scan, selective_scan_conv
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +162,40 @@ def test_autograd_conv_matches_oracle(case, dtype):
     want = {"x": dx, "conv_w": dcw, "conv_b": dcb, "delta": w["ddelta"], "A": w["dA"], "B": w["dB"],
             "C": w["dC"], "D": w["dD"], "z": w["dz"], "delta_bias": w["ddelta_bias"], "h0": w["dh0"]}
     check({k: p[k].grad for k in CONV_NAMES}, want, dtype, str(case))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_autograd_scan_then_out_proj(dtype):
+    """The tail of the block in one graph: the gated scan, then the output
+    projection, then a loss on the projected tokens.  The gradients of the
+    scan inputs and of W against the oracle chain (projection gradients,
+    then the scan's gradients for that dy)."""
+    b, d, n, L, sc = 2, 48, 16, 130, 64
+    inp, _, _ = make(b, d, n, L, dtype, seed=77, with_h0=False)
+    Wt = workloads.make_proj_inputs(1, d, d // 2, 1, dtype=dtype, device=DEV, seed=5)["W"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    R = torch.randn((b, L, d // 2), generator=g, device=DEV).to(dtype)
+    names = ("u", "delta", "B", "C", "z")
+    p = leaves(inp, names)
+    W = Wt.detach().clone().requires_grad_(True)
+    y, _ = selective_scan(p["u"], p["delta"], inp["A"], p["B"], p["C"], inp["D"], p["z"], inp["delta_bias"],
+                          delta_softplus=True, state_chunk=sc)
+    out = out_proj(y, W)
+    (out.float() * R.float()).sum().backward()
+    torch.cuda.synchronize(DEV)
+    # oracle chain, on the stored (rounded) y the projection saw
+    dy_ref, dW_ref = ref.out_proj_bwd(y.detach(), Wt, R)
+    want = ref.selective_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                                  delta_bias=inp["delta_bias"], delta_softplus=True, dy=dy_ref)
+    want = {"u": want["du"], "delta": want["ddelta"], "B": want["dB"], "C": want["dC"], "z": want["dz"]}
+    bound = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    assert rel_err(_host(W.grad), dW_ref) <= bound
+    if dtype == torch.float32:
+        check({k: p[k].grad for k in names}, want, dtype, "scan+proj")
+    else:
+        # the scan's backward sees dy rounded to bfloat16 (one 2^-9 relative
+        # rounding per element); that enters every gradient, so the bfloat16
+        # bound holds for all of them
+        for k in names:
+            assert rel_err(_host(p[k].grad), want[k]) <= 2e-2, k

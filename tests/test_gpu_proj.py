@@ -101,3 +101,68 @@ def test_out_proj_full_size_sampled(name):
     got = np.stack([out[b, t].float().cpu().numpy() for b, t in pairs])
     e = rel_err(got, want)
     assert e <= tol(w.torch_dtype), f"{name}: rel err {e:.3g}"
+
+
+# ------------------------------------------------------------------ gradients
+
+def _bwd_inputs(b, dk, dm, L, dtype, seed):
+    inp = workloads.make_proj_inputs(b, dk, dm, L, dtype=dtype, device=DEV, seed=seed)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed + 7)
+    inp["dout"] = torch.randn((b, L, dm), generator=g, device=DEV).to(dtype).contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"b{c[0]}k{c[1]}m{c[2]}L{c[3]}" for c in CASES])
+def test_out_proj_bwd_matches_oracle(case, dtype):
+    """dy and dW against the float64 gradient oracle (ragged sizes; with
+    several batch rows the dW sum is split over workgroups and reduced)."""
+    b, dk, dm, L = case
+    print(f"[proj bwd] {case} {dtype}", flush=True)
+    inp = _bwd_inputs(b, dk, dm, L, dtype, seed=3 * sum(case))
+    dy, dW = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"])
+    torch.cuda.synchronize(DEV)
+    want_dy, want_dW = ref.out_proj_bwd(inp["y"], inp["W"], inp["dout"])
+    e1 = rel_err(dy.float().cpu().numpy(), want_dy)
+    e2 = rel_err(dW.float().cpu().numpy(), want_dW)
+    assert e1 <= tol(dtype) and e2 <= tol(dtype), f"{case}: dy {e1:.3g} dW {e2:.3g}"
+
+
+def test_out_proj_bwd_one_output_and_repeatability():
+    """dy alone and dW alone give what the joint call gives; dW (split over
+    the batch rows and summed in a fixed order) is bitwise repeatable."""
+    inp = _bwd_inputs(4, 320, 136, 200, torch.bfloat16, seed=21)
+    dy, dW = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"])
+    dy1, none1 = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"], want_dW=False)
+    none2, dW1 = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"], want_dy=False)
+    _, dW2 = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"], want_dy=False)
+    torch.cuda.synchronize(DEV)
+    assert none1 is None and none2 is None
+    assert torch.equal(dy, dy1) and torch.equal(dW, dW1) and torch.equal(dW1, dW2)
+
+
+@pytest.mark.parametrize("name", ["130m", "1.4b"])
+def test_out_proj_bwd_full_size_sampled(name):
+    """The layer shapes, the launches the benchmark times: 24 sampled (batch
+    row, channel) rows of dy and 24 sampled rows of dW, every element of each,
+    against the oracle's definition evaluated for those rows."""
+    w = workloads.WORKLOADS[name]
+    dm = workloads.d_model_of(w)
+    print(f"[proj bwd full] {name}", flush=True)
+    inp = _bwd_inputs(w.batch, w.dim, dm, w.L, w.torch_dtype, seed=0)
+    dy, dW = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], inp["dout"])
+    torch.cuda.synchronize(DEV)
+    rng = np.random.default_rng(1)
+    W_h = inp["W"].double().cpu().numpy()
+    rows = [(int(rng.integers(w.batch)), int(rng.integers(w.dim))) for _ in range(24)]
+    got = np.stack([dy[b, k].double().cpu().numpy() for b, k in rows])
+    want = np.stack([W_h[:, k] @ inp["dout"][b].double().cpu().numpy().T for b, k in rows])
+    e1 = rel_err(got, want)
+    ms = [int(v) for v in rng.integers(dm, size=24)]
+    dout_h = [inp["dout"][b].double().cpu().numpy() for b in range(w.batch)]
+    y_h = [inp["y"][b].double().cpu().numpy() for b in range(w.batch)]
+    want_w = np.stack([sum(dout_h[b][:, m] @ y_h[b].T for b in range(w.batch)) for m in ms])
+    got_w = np.stack([dW[m].double().cpu().numpy() for m in ms])
+    e2 = rel_err(got_w, want_w)
+    assert e1 <= tol(w.torch_dtype) and e2 <= tol(w.torch_dtype), f"{name}: dy {e1:.3g} dW {e2:.3g}"
