@@ -107,6 +107,43 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   const int64_t b = chc / dim;
   const int64_t d = chc - b * dim;
 
+  // Every load first: the state (the bulk of the traffic) and the step's
+  // inputs are in flight together, and only then are the conv state and
+  // the SSM state stored (the stores may overwrite what was loaded: the
+  // update may be in place).
+  const int64_t n0 = 4 * q;
+  const bool has_states = valid && n0 < N;
+  const int64_t so = ch * N + n0;
+  float h[4], bv[4], cv[4], av[4];
+  if (has_states) {
+    if constexpr (VEC4) {
+      const float4 hs = *reinterpret_cast<const float4*>(a.state_in + so);
+      const float4 as = *reinterpret_cast<const float4*>(a.A + d * N + n0);
+      h[0] = hs.x; h[1] = hs.y; h[2] = hs.z; h[3] = hs.w;
+      av[0] = as.x; av[1] = as.y; av[2] = as.z; av[3] = as.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bv[e] = IO::ld(a.B + b * N + n0 + e);
+        cv[e] = IO::ld(a.C + b * N + n0 + e);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = n0 + e < N;
+        h[e] = ok ? a.state_in[so + e] : 0.0f;
+        av[e] = ok ? a.A[d * N + n0 + e] : 0.0f;
+        bv[e] = ok ? IO::ld(a.B + b * N + n0 + e) : 0.0f;
+        cv[e] = ok ? IO::ld(a.C + b * N + n0 + e) : 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = av[e] = bv[e] = cv[e] = 0.0f;
+  }
+  const float x = IO::ld(a.dlt + chc) + (a.bias != nullptr ? a.bias[d] : 0.0f);
+  const float Dd = a.D != nullptr ? a.D[d] : 0.0f;
+  const float zz = a.z != nullptr ? IO::ld(a.z + chc) : 0.0f;
+
   float uu;
   if constexpr (CONV) {
     const int K = a.conv_k;
@@ -116,14 +153,17 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
     const float xt = IO::ld(a.u + chc);
     const bool own = valid && q < K - 1;
     const float sq = own ? a.cs_in[chc * (K - 1) + q] : 0.0f;
-    const float s0 = quad_bcast<0>(sq), s1 = quad_bcast<1>(sq), s2 = quad_bcast<2>(sq);
-    // window oldest first: state[0 .. K-2], then x_t
     float pre = a.conv_b != nullptr ? a.conv_b[d] : 0.0f;
     const float* w = a.conv_w + d * K;
-    if (K >= 2) pre = __builtin_fmaf(w[0], s0, pre);
-    if (K >= 3) pre = __builtin_fmaf(w[1], s1, pre);
-    if (K >= 4) pre = __builtin_fmaf(w[2], s2, pre);
-    pre = __builtin_fmaf(w[K - 1], xt, pre);
+    float wk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wk[j] = j < K ? w[j] : 0.0f;
+    const float s0 = quad_bcast<0>(sq), s1 = quad_bcast<1>(sq), s2 = quad_bcast<2>(sq);
+    // window oldest first: state[0 .. K-2], then x_t
+    if (K >= 2) pre = __builtin_fmaf(wk[0], s0, pre);
+    if (K >= 3) pre = __builtin_fmaf(wk[1], s1, pre);
+    if (K >= 4) pre = __builtin_fmaf(wk[2], s2, pre);
+    pre = __builtin_fmaf(wk[K - 1], xt, pre);
     uu = pre * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * pre));
     // the window moves by one: element q takes element q+1, the last x_t
     const float next = quad_shift_down(sq);
@@ -132,7 +172,6 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   } else {
     uu = IO::ld(a.u + chc);
   }
-  const float x = IO::ld(a.dlt + chc) + (a.bias != nullptr ? a.bias[d] : 0.0f);
   float dt = x;
   if (a.softplus) {
     // softplus(x) = log(1 + e^x), computed as ln2 * log2(1 + 2^(x log2 e));
@@ -144,55 +183,24 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   const float dt2 = dt * kLog2e;
 
   float part = 0.0f;
-  const int64_t n0 = 4 * q;
-  const float* state_in = a.state_in;
-  float* state_out = a.state_out;
-  const float* A = a.A;
-  const typename IO::T* B = a.B;
-  const typename IO::T* C = a.C;
-  if (valid && n0 < N) {
-    const int64_t so = ch * N + n0;
-    float h[4], bv[4], cv[4], av[4];
-    if constexpr (VEC4) {
-      const float4 hs = *reinterpret_cast<const float4*>(state_in + so);
-      const float4 as = *reinterpret_cast<const float4*>(A + d * N + n0);
-      h[0] = hs.x; h[1] = hs.y; h[2] = hs.z; h[3] = hs.w;
-      av[0] = as.x; av[1] = as.y; av[2] = as.z; av[3] = as.w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bv[e] = IO::ld(B + b * N + n0 + e);
-        cv[e] = IO::ld(C + b * N + n0 + e);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = n0 + e < N;
-        h[e] = ok ? state_in[so + e] : 0.0f;
-        av[e] = ok ? A[d * N + n0 + e] : 0.0f;
-        bv[e] = ok ? IO::ld(B + b * N + n0 + e) : 0.0f;
-        cv[e] = ok ? IO::ld(C + b * N + n0 + e) : 0.0f;
-      }
-    }
+  if (has_states) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       h[e] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt2 * av[e]), h[e], dtu * bv[e]);
       part = __builtin_fmaf(cv[e], h[e], part);
     }
     if constexpr (VEC4) {
-      *reinterpret_cast<float4*>(state_out + so) = make_float4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<float4*>(a.state_out + so) = make_float4(h[0], h[1], h[2], h[3]);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (n0 + e < N) state_out[so + e] = h[e];
+        if (n0 + e < N) a.state_out[so + e] = h[e];
     }
   }
   const float tot = quad_sum(part);
   if (valid && q == 0) {
-    float yv = tot + (a.D != nullptr ? a.D[d] : 0.0f) * uu;
-    if (a.z != nullptr) {
-      const float zz = IO::ld(a.z + chc);
-      yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * zz));
-    }
+    float yv = tot + Dd * uu;
+    if (a.z != nullptr) yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * zz));
     IO::st(a.y + chc, yv);
   }
 }
