@@ -106,6 +106,15 @@ MEASURED_PROJ_TRAFFIC = {
 }
 
 
+# The same for the decode step (ssm_step.hip), keyed by workload and conv taps.
+MEASURED_DECODE_TRAFFIC = {
+    ("1.4b", 1024, 0): {"digest": "fab200ff92f6bbae", "fetch_bytes": 294450483, "write_bytes": 276824064,
+                        "profile": "profiles/ssm_step_kernel_decode1024_1.4b_bf16.md"},
+    ("1.4b", 1024, 4): {"digest": "fab200ff92f6bbae", "fetch_bytes": 344916801, "write_bytes": 327155739,
+                        "profile": "profiles/ssm_step_kernel_decode1024_conv4_1.4b_bf16.md"},
+}
+
+
 def kernel_digest(sources=("ssm_fwd.hip", "ssm_device.h")) -> str:
     """sha256 over the source of the given kernels (default: the forward scan)
     and the compiler flags they are built with: a stored traffic figure holds
@@ -148,6 +157,13 @@ def calibrate_copy(args):
     print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                       "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(2 * COPY_BYTES / ms / 1e6, 1)}),
           flush=True)
+
+
+def decode_traffic(workload: str, batch: int, conv_k: int):
+    ent = MEASURED_DECODE_TRAFFIC.get((workload, batch, conv_k))
+    if not ent or ent["digest"] != kernel_digest(("ssm_step.hip",)):
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
 
 
 def decode_bench(args):
@@ -200,13 +216,46 @@ def decode_bench(args):
     if K:  # conv state read and written, conv weights and bias
         bytes_alg += 8 * nbd * (K - 1) + 4 * w.dim * (K + 1)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
-    print(json.dumps({"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
-                      "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-                      "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-                      "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)", "data": "synthetic",
-                      "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
-                                 "d_state": w.dstate, "io_dtype": w.dtype, **({"conv_k": K} if K else {})},
-                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg}), flush=True)
+    res = {"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
+           "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)",
+           "data": "synthetic (seeded; the workload's value recipes, one step)",
+           "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
+                      "d_state": w.dstate, "io_dtype": w.dtype, **({"conv_k": K} if K else {})},
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(w0.name, w.batch, K)},
+           "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "algorithmic_bytes": bytes_alg}}
+    if args.cpu_seconds > 0:
+        # the oracle's step (its scan over L = 1 from the state, after its
+        # causal conv with the conv state prepended when there is one) on
+        # whole batch rows, as many as fit the budget, scaled to GB/s
+        from oracle import ref
+        import numpy as np
+        host = lambda t: None if t is None else t.detach().cpu()
+        rows, spent = 1, 0.0
+        while True:
+            sl = slice(0, rows)
+            t0 = time.perf_counter()
+            uu = host(u[sl])[..., None]
+            if K:
+                xs = uu if conv_state is None else torch.cat([host(conv_state[sl]), uu.float()], dim=-1)
+                uu = ref.causal_conv1d(xs, host(conv_w), host(conv_b))[..., -1:]
+            ref.selective_scan_fwd(uu, host(dl[sl])[..., None], host(inp["A"]), host(B[sl])[..., None],
+                                   host(C[sl])[..., None], host(inp["D"]),
+                                   None if z is None else host(z[sl])[..., None], host(inp["delta_bias"]),
+                                   w.softplus, h0=host(state[sl]))
+            spent = time.perf_counter() - t0
+            if spent > args.cpu_seconds / 4 or rows >= w.batch:
+                break
+            rows = min(4 * rows, w.batch)
+        res["cpu_baseline"] = {"value": round(bytes_alg * rows / w.batch / spent / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {w.batch} sequences, one step (float64 NumPy, elementwise "
+                                         "operations on one thread)"}
+    print(json.dumps(res), flush=True)
 
 
 # Backward roofline: the arithmetic the chunked recomputation cannot avoid
