@@ -70,6 +70,9 @@ def parse():
                         "(the workload's u is taken as the conv input x)")
     p.add_argument("--conv-u-out", action="store_true",
                    help="with --conv, also write u = silu(conv1d(x))")
+    p.add_argument("--affine", action="store_true",
+                   help="time the bare affine_scan primitive over the workload's recurrence chains "
+                        "(rows = b * d_inner * d_state, float32, both outputs)")
     p.add_argument("--out-proj", action="store_true",
                    help="time the output projection after the scan (ssm_out_proj, matrix cores) at the "
                         "workload's layer shape: d_inner -> d_model = d_inner / 2")
@@ -412,6 +415,71 @@ def blas_threads() -> int:
     return 1
 
 
+def affine_bench(args):
+    """One affine_scan launch per step over rows = b * d_inner * d_state
+    chains of L steps of the workload (float32 a in (0, 1], b ~ N(0,1)),
+    writing both the products and the states; inputs resident in HBM."""
+    import torch
+    import selective_state_space_ssm_amd as ssm
+    import workloads
+    from oracle import ref
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    rows, L = w.batch * w.dim * w.dstate, w.L
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.rand((rows, L), generator=g, device=dev)
+    b = torch.randn((rows, L), generator=g, device=dev)
+    oa = torch.empty_like(a)
+    ob = torch.empty_like(b)
+
+    def step():
+        ssm.affine_scan(a, b, out_a=oa, out_b=ob)
+
+    warm = max(3, args.warmup // 10)
+    steps = max(1, args.steps // 4)
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev0.elapsed_time(ev1) / steps
+    bytes_alg = 16 * rows * L                    # a, b read; out_a, out_b written; float32
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    res = {"metric": "affine_scan GB/s (a, b in; products and states out)", "value": round(gbs, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded: a ~ U(0,1), b ~ N(0,1))",
+           "config": {"workload": w.name + "-affine", "rows": rows, "seq_len": L},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+           "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "algorithmic_bytes": bytes_alg}}
+    if args.cpu_seconds > 0:
+        # the oracle's serial float64 fold (vectorised over rows) on a
+        # bounded number of whole rows, scaled to GB/s
+        nr, spent = 64, 0.0
+        while True:
+            ah, bh = a[:nr].cpu(), b[:nr].cpu()
+            t0 = time.perf_counter()
+            ref.affine_scan(ah, bh)
+            spent = time.perf_counter() - t0
+            if spent > args.cpu_seconds / 4 or nr >= rows:
+                break
+            nr = min(4 * nr, rows)
+        res["cpu_baseline"] = {"value": round(16 * nr * L / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{nr} of {rows} rows x {L} steps (float64 NumPy serial fold, "
+                                         "elementwise operations on one thread)"}
+    print(json.dumps(res), flush=True)
+
+
 def proj_traffic(workload: str):
     ent = MEASURED_PROJ_TRAFFIC.get(workload)
     if not ent or ent["digest"] != kernel_digest(("ssm_proj.hip", "ssm_device.h")):
@@ -567,6 +635,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.affine:
+        affine_bench(args)
         return
     if args.out_proj:
         proj_bench(args)
