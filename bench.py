@@ -586,14 +586,16 @@ def proj_bench(args):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(inp, w, budget_s):
+def cpu_baseline(inp, w, budget_s, threads=0):
     """The float64 C oracle, as it is, on a bounded sample of whole channels
-    of the same workload; throughput scaled to the workload's GB/s."""
+    of the same workload; throughput scaled to the workload's GB/s.  threads
+    0: every core the process may use (OMP_NUM_THREADS if set)."""
     import numpy as np
     from oracle import build as ob, cpu
     if not os.path.exists(ob.LIB):
         ob.build()
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    if threads <= 0:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     rows_total = w.batch * w.dim
     host = {k: (v.float().cpu().numpy() if hasattr(v, "cpu") else v)
             for k, v in inp.items() if k in ("u", "delta", "z", "A", "B", "C", "D", "delta_bias")}
@@ -724,6 +726,38 @@ def main():
 
     bytes_alg = w.algorithmic_bytes() + extra_bytes
     gbs = bytes_alg / (ms * 1e-3) / 1e9
+
+    # Cold-cache timing: before each of 20 single launches, a 512 MiB write
+    # evicts the 256 MB Infinity Cache; the median launch time is reported.
+    # And the device's streaming-copy rate in the same run: 1 GiB copied
+    # device to device, read + write bytes over the time.
+    scrub = torch.empty(1 << 27, device=dev, dtype=torch.float32)
+    cold = []
+    for r in range(20):
+        scrub.fill_(float(r))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        cold.append(e0.elapsed_time(e1))
+    cold.sort()
+    ms_cold = cold[len(cold) // 2]
+    del scrub
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
     plan = ssm.plan_for(w.batch, w.dim, w.dstate, w.L, w.dtype)
     if args.plan != "auto":
         plan["plan"] = args.plan
@@ -755,11 +789,15 @@ def main():
         "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "algorithmic_bytes": bytes_alg},
+        "cold": {"ms_per_step": round(ms_cold, 5), "value": round(bytes_alg / (ms_cold * 1e-3) / 1e9, 2),
+                 "unit": "GB/s", "note": "median of 20 single launches, each after a 512 MiB write"},
+        "hbm_copy_gbs": round(copy_gbs, 1),
     }
     if w.dtype == "bf16":
         out["dtype"] = "f32 (bf16 storage)"
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        out["cpu_baseline_1core"] = cpu_baseline(inp, w, args.cpu_seconds / 4, threads=1)
     print(json.dumps(out), flush=True)
 
 
