@@ -102,9 +102,9 @@ MEASURED_TRAFFIC = {
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "94bbcc5602b20956", "fetch_bytes": 187067505, "write_bytes": 50337168,
+    "130m": {"digest": "ad29999056560c91", "fetch_bytes": 187093991, "write_bytes": 50339312,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
-    "1.4b": {"digest": "94bbcc5602b20956", "fetch_bytes": 404032254, "write_bytes": 82881544,
+    "1.4b": {"digest": "ad29999056560c91", "fetch_bytes": 404022732, "write_bytes": 83096608,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_1.4b_bf16.md"},
 }
 

@@ -179,12 +179,20 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) 
     const int64_t rr = p.K - k0;
     return rr < 0 ? -1 : (rr > BK ? BK : static_cast<int>(rr));
   };
-  // step s of this workgroup: segment seg0 + s / ksteps, k0 = (s % ksteps) * BK
+  // The steps of this workgroup walk K in BK steps within a segment, then
+  // the next segment; (cur_seg, cur_k0) is the next step to load, advanced
+  // by one step per load (no 64-bit division in the loop).
   const int64_t ksteps = (p.K + BK - 1) / BK;
   const int64_t nsteps = (seg1 - seg0) * ksteps;
-  auto load_global = [&](int64_t s) {
-    const int64_t seg = seg0 + s / ksteps;
-    const int64_t k0 = (s % ksteps) * BK;
+  int64_t cur_seg = seg0, cur_k0 = 0;
+  auto load_global = [&]() {
+    const int64_t seg = cur_seg;
+    const int64_t k0 = cur_k0;
+    cur_k0 += BK;
+    if (cur_k0 >= ksteps * BK) {
+      cur_k0 = 0;
+      ++cur_seg;
+    }
     const Rsrc ra = make_rsrc(p.a + (bt * p.a_batch + seg * p.a_seg) * ES, abytes);
     const Rsrc rb = make_rsrc(p.b + (bt * p.b_batch + seg * p.b_seg) * ES, bbytes);
     const int krem = krem_of(k0);
@@ -333,13 +341,13 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) 
   };
 
   if (nsteps > 0) {
-    load_global(0);
+    load_global();
     store_lds(0);
   }
   __syncthreads();
   for (int64_t s = 0; s < nsteps; ++s) {
     const bool more = s + 1 < nsteps;
-    if (more) load_global(s + 1);
+    if (more) load_global();
     compute(static_cast<int>(s & 1));
     if (more) store_lds(static_cast<int>((s + 1) & 1));
     __syncthreads();
