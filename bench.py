@@ -118,6 +118,18 @@ MEASURED_DECODE_TRAFFIC = {
 }
 
 
+# The same for the backward kernel (ssm_bwd.hip), keyed by workload and
+# conv taps, at the default state_chunk (128) and states per lane (auto).
+MEASURED_BWD_TRAFFIC = {
+    ("130m", 0): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 518590206, "write_bytes": 580762560,
+                  "profile": "profiles/ssm_bwd_kernel_130m_f32.md"},
+    ("1.4b", 0): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 1127958592, "write_bytes": 1248096728,
+                  "profile": "profiles/ssm_bwd_kernel_1.4b_bf16.md"},
+    ("130m", 4): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 620653493, "write_bytes": 595324352,
+                  "profile": "profiles/ssm_bwd_kernel_conv4_130m_f32.md"},
+}
+
+
 def kernel_digest(sources=("ssm_fwd.hip", "ssm_device.h")) -> str:
     """sha256 over the source of the given kernels (default: the forward scan)
     and the compiler flags they are built with: a stored traffic figure holds
@@ -272,6 +284,14 @@ BWD_FLOP_PER_STATE_STEP = 20.0
 BWD_ALU_PEAK_TFLOPS = LANE_SLOTS_PER_S / BWD_SLOTS_PER_STATE_STEP * BWD_FLOP_PER_STATE_STEP / 1e12
 
 
+def bwd_traffic(workload: str, conv_k: int, state_chunk: int, states_per_lane: int):
+    ent = MEASURED_BWD_TRAFFIC.get((workload, conv_k))
+    if (not ent or state_chunk != 128 or states_per_lane != 0
+            or ent["digest"] != kernel_digest(("ssm_bwd.hip", "ssm_device.h"))):
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
+
+
 def bwd_algorithmic_bytes(w, state_chunk: int) -> int:
     """Every input of the backward read once (u, delta, z, dy, B, C, A, D,
     bias, the chunk states, dlast) and every gradient written once (du,
@@ -391,9 +411,12 @@ def bwd_bench(args):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(BWD_ALU_PEAK_TFLOPS, 2),
-                     "unit": "TFLOP/s", "frac": round(tflops / BWD_ALU_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / BWD_ALU_PEAK_TFLOPS, 4),
+                     "traffic": bwd_traffic(w.name, K, sc, args.states_per_lane)},
         "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": bytes_alg},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": bwd_traffic(w.name, K, sc, args.states_per_lane),
+                         "algorithmic_bytes": bytes_alg},
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = bwd_cpu_baseline(inp, gr, w, args.cpu_seconds)
