@@ -97,6 +97,16 @@ MEASURED_TRAFFIC = {
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
     "1.4b": {"digest": "d95ae7d777032fe9", "plan": "carry", "fetch_bytes": 441692321, "write_bytes": 166576723,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
+    "varlen": {"digest": "d95ae7d777032fe9", "plan": "carry", "fetch_bytes": 6473141997, "write_bytes": 1574714222,
+               "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
+    "130m+conv4": {"digest": "d95ae7d777032fe9", "plan": "mixed", "fetch_bytes": 335528656, "write_bytes": 101450304,
+                   "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
+}
+
+# The same for the bare affine scan (affine_scan.hip), keyed by workload.
+MEASURED_AFFINE_TRAFFIC = {
+    "130m": {"digest": "fb9d6e51286ff07f", "fetch_bytes": 3221436849, "write_bytes": 3227328896,
+             "profile": "profiles/affine_scan_kernel_130m_chains.md"},
 }
 
 
@@ -438,6 +448,13 @@ def blas_threads() -> int:
     return 1
 
 
+def affine_traffic(workload: str):
+    ent = MEASURED_AFFINE_TRAFFIC.get(workload)
+    if not ent or ent["digest"] != kernel_digest(("affine_scan.hip",)):
+        return None
+    return int(ent["fetch_bytes"] + ent["write_bytes"])
+
+
 def affine_bench(args):
     """One affine_scan launch per step over rows = b * d_inner * d_state
     chains of L steps of the workload (float32 a in (0, 1], b ~ N(0,1)),
@@ -481,7 +498,7 @@ def affine_bench(args):
            "data": "synthetic (seeded: a ~ U(0,1), b ~ N(0,1))",
            "config": {"workload": w.name + "-affine", "rows": rows, "seq_len": L},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": affine_traffic(w.name)},
            "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "algorithmic_bytes": bytes_alg}}
     if args.cpu_seconds > 0:
@@ -785,7 +802,8 @@ def main():
     if args.plan != "auto":
         plan["plan"] = args.plan
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
-    traffic = None if (use_states or args.conv) else measured_traffic(w.name, plan)
+    key = w.name + (f"+conv{args.conv}" if args.conv else "")
+    traffic = None if (use_states or args.conv_u_out) else measured_traffic(key, plan)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
