@@ -70,6 +70,9 @@ def parse():
                         "(the workload's u is taken as the conv input x)")
     p.add_argument("--conv-u-out", action="store_true",
                    help="with --conv, also write u = silu(conv1d(x))")
+    p.add_argument("--graph", type=int, default=0, metavar="G",
+                   help="with --decode: capture G consecutive steps in one HIP graph and time its replays "
+                        "(per step: replay time / G; the form a serving loop would use)")
     p.add_argument("--affine", action="store_true",
                    help="time the bare affine_scan primitive over the workload's recurrence chains "
                         "(rows = b * d_inner * d_state, float32, both outputs)")
@@ -225,15 +228,32 @@ def decode_bench(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    run, per_run = step, 1
+    if args.graph > 0:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.graph):
+                step()
+        run, per_run = graph.replay, args.graph
+        for _ in range(max(1, args.warmup // per_run)):
+            run()
+        torch.cuda.synchronize(dev)
+    nrun = max(1, args.steps // per_run)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for _ in range(nrun):
+        run()
     ev1.record(stream)
     torch.cuda.synchronize(dev)
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev0.elapsed_time(ev1) / (nrun * per_run)
     es = 4 if w.dtype == "f32" else 2
     nbd = w.batch * w.dim
     bytes_alg = (8 * nbd * w.dstate + nbd * es * (3 + int(w.gated)) + 2 * w.batch * w.dstate * es
@@ -242,12 +262,13 @@ def decode_bench(args):
         bytes_alg += 8 * nbd * (K - 1) + 4 * w.dim * (K + 1)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     res = {"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
-           "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": nrun * per_run,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)",
            "data": "synthetic (seeded; the workload's value recipes, one step)",
            "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
-                      "d_state": w.dstate, "io_dtype": w.dtype, **({"conv_k": K} if K else {})},
+                      "d_state": w.dstate, "io_dtype": w.dtype, **({"conv_k": K} if K else {}),
+                      **({"hip_graph_steps": args.graph} if args.graph else {})},
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_alg,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(w0.name, w.batch, K)},
