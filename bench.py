@@ -590,7 +590,10 @@ def proj_bench(args):
     flop = 2.0 * w.batch * w.L * dm * w.dim * passes
     tflops = flop / (ms * 1e-3) / 1e12
     es = 4 if w.dtype == "f32" else 2
-    bytes_alg = es * (w.batch * w.dim * w.L + dm * w.dim + w.batch * w.L * dm) * (5 if args.bwd else 3) // 3
+    if args.bwd:   # y, W and dout read; dy and dW written
+        bytes_alg = es * (2 * w.batch * w.dim * w.L + 2 * dm * w.dim + w.batch * w.L * dm)
+    else:          # y and W read; out written
+        bytes_alg = es * (w.batch * w.dim * w.L + dm * w.dim + w.batch * w.L * dm)
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     res = {
         "metric": ("output projection backward TFLOP/s (dy and dW: 4 b L d_model d_inner per step)" if args.bwd
