@@ -306,3 +306,24 @@ def test_large_batch_or_width(b, d, L):
     idx = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
     assert rel_err(_host(y[idx]), y_ref) <= 2e-2
     assert rel_err(_host(last[idx]), last_ref) <= 1e-4
+
+
+def test_longest_accepted_sequence():
+    """L at the library's limit, (2^32 - 4096) / 64 = 67108800 steps, with
+    one 16-channel group and 16 states: the last channel's row of u, delta
+    and y and the last state's row of B and C end 4096 bytes short of 2^32,
+    the top of the 32-bit offsets the kernels address rows with.  Channels 0
+    and 15 against the C oracle over every step (L + 1 is refused, see the
+    host tests)."""
+    L = ((1 << 32) - 4096) // 64
+    inp = small_inputs(1, 16, 16, L, gated=False, seed=23)
+    print(f"[max L] L={L} plan {ssm.plan_for(1, 16, 16, L, 'f32')}", flush=True)
+    y, last = run_gpu(inp)
+    rb, rd = np.array([0, 0]), np.array([0, 15])
+    y_ref, last_ref = oracle_rows(inp, rb, rd)
+    idx = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    assert rel_err(_host(last[idx]), last_ref) <= 1e-4
+    for i in range(2):
+        assert rel_err(_host(y[idx][i]), y_ref[i]) <= 1e-4, f"channel {rd[i]}"
+    del inp, y, last
+    torch.cuda.empty_cache()
