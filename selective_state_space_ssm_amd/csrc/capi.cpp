@@ -199,8 +199,10 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
 
   if (pl == SSM_PLAN_MIXED) {
     a.chunk = L;
+    // one two-group block per three groups, the rest one-group blocks; with
+    // fewer than three groups (a forced mixed plan) every block has one group
     const int64_t gd = ceil_div(dim, kGroup);
-    hipError_t e = ssm::launch_mixed_full(a, bf16, gd / 3 > 0 ? gd / 3 : 1, 1, st);
+    hipError_t e = ssm::launch_mixed_full(a, bf16, gd / 3, 1, st);
     if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
     return SSM_OK;
   }

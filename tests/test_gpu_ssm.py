@@ -122,13 +122,15 @@ def test_ragged_shapes(shape, dtype):
     check_all(inp)
 
 
-@pytest.mark.parametrize("shape", [(1, 64, 16, 100), (2, 130, 16, 257), (3, 200, 5, 1000), (1, 48, 16, 64)],
+@pytest.mark.parametrize("shape", [(1, 64, 16, 100), (2, 130, 16, 257), (3, 200, 5, 1000), (1, 48, 16, 64),
+                                   (2, 16, 16, 100), (3, 20, 7, 45)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_mixed_plan(shape, dtype):
     """Blocks of two 16-channel groups at two states per lane next to blocks
     of one group at one state per lane (ragged channel and step tails
-    included) give the oracle's result."""
+    included) give the oracle's result; with fewer than three groups every
+    block has one group."""
     inp = small_inputs(*shape, dtype=dtype, seed=3 + sum(shape))
     check_all(inp, plan="mixed")
 
