@@ -1,9 +1,11 @@
-"""Seeded random sweep over the forward, the start-state / chunk-state forward
-and the backward: sizes, dtypes, optional inputs, plans and states per lane
+"""Seeded random sweep over every entry point (forward plans, start states and
+chunk states, backward, the conv in front forward and backward, decode steps
+with and without the conv, the output projection and its gradients, the
+affine scan): sizes, dtypes, optional inputs, plans and states per lane
 drawn from fixed generators, every element of every output compared with
-the C oracle (float64).  The cases are small (the oracle finishes each in
-milliseconds) but span several 16-channel groups, 32-step tiles and chunks
-with ragged ends, n < 16 and L = 1.
+the float64 oracle (the affine scan bit for bit with its float32 replay).  The cases are small (the oracle finishes each in
+milliseconds) but span several 16-channel groups, 32-step tiles, chunks and
+matrix tiles with ragged ends, n < 16 and L = 1.
 
 Bounds as in the per-entry-point tests: max |gpu - oracle| / max |oracle|
 <= 1e-4 for float32 results and 2e-2 for bfloat16-stored ones.
@@ -14,7 +16,7 @@ import torch
 
 import selective_state_space_ssm_amd as ssm
 import workloads
-from oracle import cpu
+from oracle import cpu, ref
 
 pytestmark = pytest.mark.gpu
 
@@ -157,3 +159,180 @@ def test_backward_sweep(c):
         bound = 2e-2 if (c["dtype"] == "bf16" and k in IO_KEYS) else 1e-4
         e = rel_err(_host(got[k]), v)
         assert e <= bound, f"{k}: {e:.3e}"
+
+
+# ------------------------------------------------------- conv1d + SiLU in front
+
+CONV = _cases(7404, 16, with_plan=True)
+
+
+@pytest.mark.parametrize("c", CONV, ids=[_id(c) for c in CONV])
+def test_conv_forward_sweep(c):
+    inp, _ = _inputs(c)
+    rng = np.random.default_rng(c["seed"] + 1)
+    K = int(rng.integers(1, 5))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(c["seed"] + 7)
+    conv_w = torch.randn((c["d"], K), generator=g, device=DEV) * (1.0 / K)
+    conv_b = torch.randn((c["d"],), generator=g, device=DEV) * 0.1 if rng.integers(2) else None
+    h0 = torch.randn((c["b"], c["d"], c["n"]), generator=g, device=DEV) if rng.integers(2) else None
+    print(f"[sweep conv] {_id(c)} K {K} bias {conv_b is not None} h0 {h0 is not None} seed {c['seed']}",
+          flush=True)
+    y, last, _, u = ssm.ssm_scan_fwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"],
+                                          conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                          delta_softplus=c["softplus"], h0=h0, plan=c["plan"], return_u=True)
+    torch.cuda.synchronize(DEV)
+    u_ref = ref.causal_conv1d(inp["u"], conv_w, conv_b)
+    y_ref, last_ref = ref.selective_scan_fwd(u_ref, inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                             inp["delta_bias"], c["softplus"], h0=h0)
+    assert rel_err(_host(u), u_ref) <= _bound(c["dtype"])
+    assert rel_err(_host(y), y_ref) <= _bound(c["dtype"])
+    assert rel_err(_host(last), last_ref) <= 1e-4
+
+
+CONV_BWD = _cases(7505, 10, with_plan=False)
+
+
+@pytest.mark.parametrize("c", CONV_BWD, ids=[_id(c) for c in CONV_BWD])
+def test_conv_backward_sweep(c):
+    inp, w = _inputs(c)
+    rng = np.random.default_rng(c["seed"] + 2)
+    K = int(rng.integers(1, 5))
+    sc = 32 * int(rng.integers(1, 17))
+    S = int(rng.choice([0, 1, 2, 4]))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(c["seed"] + 8)
+    conv_w = torch.randn((c["d"], K), generator=g, device=DEV) * (1.0 / K)
+    conv_b = torch.randn((c["d"],), generator=g, device=DEV) * 0.1 if rng.integers(2) else None
+    h0 = torch.randn((c["b"], c["d"], c["n"]), generator=g, device=DEV) if rng.integers(2) else None
+    gr = workloads.make_grads(w, device=DEV, seed=c["seed"])
+    dlast = gr["dlast"] if rng.integers(2) else None
+    print(f"[sweep conv bwd] {_id(c)} K {K} state_chunk {sc} S {S} seed {c['seed']}", flush=True)
+    x = inp["u"]
+    _, _, cs, _ = ssm.ssm_scan_fwd_conv(x, conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], conv_b=conv_b,
+                                        D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                        delta_softplus=c["softplus"], h0=h0, state_chunk=sc)
+    got = ssm.ssm_scan_bwd_conv(x, conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, gr["dy"],
+                                conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                delta_softplus=c["softplus"], h0=h0, dlast=dlast, states_per_lane=S)
+    torch.cuda.synchronize(DEV)
+    u = ref.causal_conv1d(x, conv_w, conv_b)
+    want = ref.selective_scan_bwd(u, inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                                  delta_bias=inp["delta_bias"], delta_softplus=c["softplus"], h0=h0, dy=gr["dy"],
+                                  dlast=dlast)
+    dx, dw, db = ref.causal_conv1d_silu_bwd(x, conv_w, conv_b, want["du"])
+    want.update(dx=dx, dconv_w=dw, dconv_b=db)
+    for k in ("dx", "dconv_w", "dconv_b", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        if want.get(k) is None or got.get(k) is None:
+            continue
+        bound = 2e-2 if (c["dtype"] == "bf16" and k in ("dx", "ddelta", "dz")) else 1e-4
+        e = rel_err(_host(got[k]), want[k])
+        assert e <= bound, f"{k}: {e:.3e}"
+
+
+# ------------------------------------------------------- decode steps
+
+STEP = _cases(7606, 12, with_plan=False)
+
+
+@pytest.mark.parametrize("c", STEP, ids=[_id(c) for c in STEP])
+def test_decode_sweep(c):
+    """T = min(L, 24) decode steps from a random state, with the conv in front
+    for half of the cases, against the oracle's scan over the same steps."""
+    inp, _ = _inputs(c)
+    T = min(c["L"], 24)
+    rng = np.random.default_rng(c["seed"] + 3)
+    K = int(rng.integers(0, 5))   # 0: no conv
+    g = torch.Generator(device=DEV)
+    g.manual_seed(c["seed"] + 9)
+    h0 = torch.randn((c["b"], c["d"], c["n"]), generator=g, device=DEV)
+    conv_w = torch.randn((c["d"], K), generator=g, device=DEV) * (1.0 / K) if K else None
+    conv_b = torch.randn((c["d"],), generator=g, device=DEV) * 0.1 if K else None
+    print(f"[sweep decode] {_id(c)} T {T} K {K} seed {c['seed']}", flush=True)
+    state = h0.clone()
+    cstate = torch.zeros((c["b"], c["d"], K - 1), device=DEV) if K > 1 else None
+    ys = []
+    for t in range(T):
+        pick = lambda v: None if v is None else v[..., t].contiguous()
+        if K:
+            y, cstate, state, _ = ssm.ssm_step_conv(pick(inp["u"]), conv_w, cstate, pick(inp["delta"]), inp["A"],
+                                                    pick(inp["B"]), pick(inp["C"]), state, conv_b=conv_b,
+                                                    D=inp["D"], z=pick(inp["z"]), delta_bias=inp["delta_bias"],
+                                                    delta_softplus=c["softplus"])
+        else:
+            y, state = ssm.ssm_step(pick(inp["u"]), pick(inp["delta"]), inp["A"], pick(inp["B"]), pick(inp["C"]),
+                                    state, D=inp["D"], z=pick(inp["z"]), delta_bias=inp["delta_bias"],
+                                    delta_softplus=c["softplus"])
+        ys.append(y.clone())
+    torch.cuda.synchronize(DEV)
+    sl = lambda v: None if v is None else v[..., :T]
+    u_ref = ref.causal_conv1d(sl(inp["u"]), conv_w, conv_b) if K else sl(inp["u"])
+    y_ref, last_ref = ref.selective_scan_fwd(u_ref, sl(inp["delta"]), inp["A"], sl(inp["B"]), sl(inp["C"]), inp["D"],
+                                             sl(inp["z"]), inp["delta_bias"], c["softplus"], h0=h0)
+    assert rel_err(np.stack([_host(v) for v in ys], -1), y_ref) <= _bound(c["dtype"])
+    assert rel_err(_host(state), last_ref) <= 1e-4
+
+
+# ------------------------------------------------------- output projection
+
+def _proj_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        out.append(dict(b=int(rng.integers(1, 5)), k=int(rng.integers(1, 700)), m=int(rng.integers(1, 400)),
+                        L=int(rng.integers(1, 600)), dtype=("f32", "bf16")[int(rng.integers(2))],
+                        seed=int(rng.integers(1 << 20))))
+    return out
+
+
+PROJ = _proj_cases(7707, 20)
+
+
+@pytest.mark.parametrize("c", PROJ, ids=[f"b{c['b']}k{c['k']}m{c['m']}L{c['L']}-{c['dtype']}" for c in PROJ])
+def test_out_proj_sweep(c):
+    dtype = torch.float32 if c["dtype"] == "f32" else torch.bfloat16
+    inp = workloads.make_proj_inputs(c["b"], c["k"], c["m"], c["L"], dtype=dtype, device=DEV, seed=c["seed"])
+    g = torch.Generator(device=DEV)
+    g.manual_seed(c["seed"] + 7)
+    dout = torch.randn((c["b"], c["L"], c["m"]), generator=g, device=DEV).to(dtype).contiguous()
+    print(f"[sweep proj] {c}", flush=True)
+    out = ssm.ssm_out_proj(inp["y"], inp["W"])
+    dy, dW = ssm.ssm_out_proj_bwd(inp["y"], inp["W"], dout)
+    torch.cuda.synchronize(DEV)
+    want_dy, want_dW = ref.out_proj_bwd(inp["y"], inp["W"], dout)
+    assert rel_err(_host(out), ref.out_proj(inp["y"], inp["W"])) <= _bound(c["dtype"])
+    assert rel_err(_host(dy), want_dy) <= _bound(c["dtype"])
+    assert rel_err(_host(dW), want_dW) <= _bound(c["dtype"])
+
+
+# ------------------------------------------------------- affine scan
+
+def _affine_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 300)), int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 20000))])),
+             int(rng.integers(1 << 20))) for _ in range(count)]
+
+
+AFFINE = _affine_cases(7808, 16)
+
+
+@pytest.mark.parametrize("rows,L,seed", AFFINE, ids=[f"r{r}L{l}" for r, l, _ in AFFINE])
+def test_affine_scan_sweep(rows, L, seed):
+    """Bit for bit against the float32 replay of the documented association
+    order (any NaN matching any NaN), for inputs with decays, growth, exact
+    zeros and subnormal-range values."""
+    g = torch.Generator().manual_seed(seed)
+    a = torch.exp(torch.randn((rows, L), generator=g) * 1.5)
+    a[torch.rand((rows, L), generator=g) < 0.01] = 0.0
+    a[torch.rand((rows, L), generator=g) < 0.01] = 1e-30
+    b = torch.randn((rows, L), generator=g)
+    a, b = a.float().contiguous(), b.float().contiguous()
+    print(f"[sweep affine] rows {rows} L {L} seed {seed}", flush=True)
+    oa, ob = ssm.affine_scan(a.to(DEV), b.to(DEV))
+    torch.cuda.synchronize(DEV)
+    o = ssm.affine_scan_order()
+    ra, rb = cpu.affine_replay_f32(a.numpy(), b.numpy(), o["items_per_lane"], o["lanes"], o["waves"])
+    for got, want in ((oa.cpu().numpy(), ra), (ob.cpu().numpy(), rb)):
+        nx, ny = np.isnan(got), np.isnan(want)
+        assert np.array_equal(nx, ny)
+        assert np.array_equal(got[~nx].view(np.uint32), np.asarray(want, np.float32)[~ny].view(np.uint32))
