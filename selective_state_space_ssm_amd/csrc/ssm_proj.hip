@@ -44,6 +44,16 @@
 //             order inside a 16-value step permuted identically for both
 //             operands so that each lane reads 4 consecutive k at once
 //
+// bfloat16 with every size a multiple of 8 (the block's shapes) takes a
+// second kernel, ssm_proj_dma_kernel, with the same tiles and results bit
+// for bit, whose staging costs no registers: both operands go from HBM
+// straight into LDS (16-byte buffer loads with the LDS as destination), four
+// 32-k stages deep, and B stays in its own [k][n] layout in LDS.  The B
+// fragments are read with gfx950's transposing LDS read (ds_read_b64_tr_b16):
+// lane s of each 16-lane group reads 4 consecutive n of k-row s / 4, and the
+// read hands lane i the 4 k values of column i.  Each step reads the next
+// step's fragments before its own MFMAs.
+//
 // When the output tiles alone would leave CUs idle (dW: d_model x d_inner
 // tiles only), the segments are split over `nsplit` workgroups per tile;
 // each writes a float32 partial and a second kernel sums the partials in a
@@ -69,6 +79,8 @@
 //   [Mamba-2 page] "Mamba (part 2): parallel scan and hardware-aware
 //                  optimisation" (scwacadex.pages.dev, blog8_mamba_parallel_scan)
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "ssm_device.h"
 #include "ssm_kernels.h"
@@ -399,6 +411,236 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) 
   }
 }
 
+// --------------------------------------------------------------------------
+// bfloat16, every size a multiple of 8: the operands DMA'd into LDS.
+//
+// Stage layout (32 KB): A [256 m][32 k] in 64-byte rows whose 16-byte chunk
+// c sits at position c ^ ((m >> 2) & 3); B [32 k][256 n] in 512-byte rows
+// whose chunk c sits at c ^ swz_kn(k).  Both make the fragment reads spread
+// over every bank: 16 lanes reading one chunk of 16 consecutive A rows, and
+// one transposing read covering 16 B rows (k = 8 g + t, t < 4) x 32 bytes.
+// A DMA load writes 16 bytes per lane at block base + 16 lane, so the
+// swizzle is applied by choosing which global chunk each lane fetches.
+// --------------------------------------------------------------------------
+constexpr int kDmaBK = 32;                       // k per stage
+constexpr int kDmaStages = 4;                    // stages in LDS (three in flight)
+constexpr int kDmaA = 256 * kDmaBK * 2;          // A bytes per stage
+constexpr int kDmaStage = 2 * kDmaA;             // A + B bytes per stage
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz_kn(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+
+// Buffer descriptor words for dma16: base, stride 0, size in bytes.
+__device__ __forceinline__ u32x4 dma_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = static_cast<uint32_t>(a);
+  d.y = static_cast<uint32_t>(a >> 32) & 0xffffu;
+  d.z = bytes;
+  d.w = static_cast<uint32_t>(kRsrcWord3);
+  return d;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff (past the size:
+// zeros) into LDS at lds + 16 * lane.  Written as inline asm so that the
+// compiler does not count it: it would otherwise wait for every load in
+// flight before the next LDS read, which undoes the pipeline.  The kernel
+// waits for these loads itself (vmcnt before the barrier of the step that
+// reads the stage, and all of them before the workgroup ends).  M0 holds
+// the LDS address; one wait state separates its write from the load that
+// reads it.  Nothing else in the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const u32x4& d, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(d)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <bool PART>
+__global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
+  constexpr int BM = 256, BN = 256, BK = kDmaBK, TI = 8, TJ = 8, ES = 2;
+  __shared__ __attribute__((aligned(1024))) char stg[kDmaStages][kDmaStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // ---- tile of this workgroup (as in ssm_proj_gemm_kernel)
+  const int64_t nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
+  const int64_t G = static_cast<int64_t>(gridDim.x);
+  const int64_t pid = blockIdx.x, q8 = G / 8, r8 = G % 8, xcd = pid % 8, slot = pid / 8;
+  const int64_t logical = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+  const int64_t mt = logical % nm;
+  int64_t rest = logical / nm;
+  const int64_t nt = rest % nn;
+  rest /= nn;
+  const int64_t split = rest % p.nsplit, bt = rest / p.nsplit;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
+  const int64_t seg0 = split * p.spp;
+  const int64_t seg1 = (seg0 + p.spp < p.nseg) ? seg0 + p.spp : p.nseg;
+
+  // ---- DMA roles: 1 KB blocks q = wave + 4 i (i < 4) of each operand per
+  // stage.  A block q: rows 16 q + lane / 4, position lane & 3.  B block q:
+  // k-rows 2 q + lane / 32, position lane & 31.  Offsets at k0 = 0.
+  const uint32_t astride = static_cast<uint32_t>(p.lda * ES), bstride = static_cast<uint32_t>(p.ldb * ES);
+  uint32_t a_off[4], b_off[4];
+  int a_k[4], b_k[4];
+  bool a_ok[4], b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave + 4 * i;
+    const int ra = 16 * q + (lane >> 2);
+    const int ca = (lane & 3) ^ ((ra >> 2) & 3);
+    a_ok[i] = m0 + ra < p.M;
+    a_k[i] = 8 * ca;
+    a_off[i] = static_cast<uint32_t>((m0 + ra) * astride) + static_cast<uint32_t>(8 * ca * ES);
+    const int rb = 2 * q + (lane >> 5);
+    const int cb = (lane & 31) ^ swz_kn(rb);
+    b_ok[i] = n0 + 8 * cb < p.N;
+    b_k[i] = rb;
+    b_off[i] = static_cast<uint32_t>(rb) * bstride + static_cast<uint32_t>((n0 + 8 * cb) * ES);
+  }
+  const uint32_t abytes = static_cast<uint32_t>(p.M * p.lda * ES);
+  const uint32_t bbytes = static_cast<uint32_t>(p.K * p.ldb * ES);
+  const int64_t ksteps = (p.K + BK - 1) / BK;
+  const int64_t nsteps = (seg1 - seg0) * ksteps;
+  // The stages are issued in order; (cur_seg, cur_k0) is the next one.  A
+  // stage past the end is still issued, all of it past the buffers (zeros),
+  // so that every step issues the same number of loads and one vmcnt value
+  // serves every wait.
+  int64_t cur_seg = seg0, cur_k0 = 0;
+  auto issue = [&](auto KS, bool live) {
+    const int64_t seg = live ? cur_seg : seg0, k0 = cur_k0;
+    if (live) {
+      cur_k0 += BK;
+      if (cur_k0 >= ksteps * BK) {
+        cur_k0 = 0;
+        ++cur_seg;
+      }
+    }
+    const u32x4 ra = dma_desc(p.a + (bt * p.a_batch + seg * p.a_seg) * ES, abytes);
+    const u32x4 rb = dma_desc(p.b + (bt * p.b_batch + seg * p.b_seg) * ES, bbytes);
+    const int64_t left = p.K - k0;
+    const int krem = !live ? -1 : (left > BK ? BK : static_cast<int>(left));
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)stg[decltype(KS)::value]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave + 4 * i;
+      const bool oka = a_ok[i] & (a_k[i] < krem);
+      dma16(ra, oka ? a_off[i] + static_cast<uint32_t>(k0 * ES) : kOOB, base + q * 1024);
+      const bool okb = b_ok[i] & (b_k[i] < krem);
+      dma16(rb, okb ? b_off[i] + static_cast<uint32_t>(k0) * bstride : kOOB, base + kDmaA + q * 1024);
+    }
+  };
+
+  // ---- fragments: A lane reads row wm*128 + 16 i + (lane & 15), chunk
+  // lane >> 4 (k 8 (lane >> 4) ..); B lane 16 g + s reads k-row 8 g + s / 4
+  // (+ 4 for k 8 g + 4 ..) at n = wn*128 + 16 j + 4 (s & 3)
+  const int a_lo = (wm * 128 + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ (((lane & 15) >> 2) & 3));
+  const int kB = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  int b_lo[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+    b_lo[j] = kB * 512 + 16 * (wn * 16 + ((2 * j) ^ swz_kn(kB)) + ((lane >> 1) & 1)) + 8 * (lane & 1);
+
+  struct Frag {
+    uint4 a[TI], b[TJ];
+  };
+  auto read_frags = [&](auto KS, Frag& f) {
+    const char* sa = stg[decltype(KS)::value];
+    const char* sb = sa + kDmaA;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const uint4*>(sa + a_lo + 1024 * i);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sb + b_lo[j]));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sb + b_lo[j] + 4 * 512));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      f.b[j] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+    }
+  };
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.a[i]), as_bf16x8(f.b[j]), acc[i][j], 0, 0, 0);
+  };
+
+  // ---- pipeline.  Step s: wait until stage s + 1 has landed (8 loads per
+  // wave per stage, so vmcnt(8) leaves only stage s + 2 in flight) and until
+  // this wave's reads issued at step s - 1 are done (lgkmcnt(0)); barrier
+  // (no fence: a release fence would wait for every load in flight); refill
+  // the stage read at step s - 1 with stage s + 3; read step s + 1's
+  // fragments; step s's MFMAs.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  constexpr int kWait16 = 0 | (7 << 4) | (0 << 8) | (1 << 14);   // vmcnt(16) lgkmcnt(0)
+  constexpr int kWait8 = 8 | (7 << 4) | (0 << 8);                // vmcnt(8) lgkmcnt(0)
+  Frag F0, F1;
+  issue(S0{}, 0 < nsteps);
+  issue(S1{}, 1 < nsteps);
+  issue(S2{}, 2 < nsteps);
+  __builtin_amdgcn_s_waitcnt(kWait16);
+  asm volatile("s_barrier" ::: "memory");
+  read_frags(S0{}, F0);
+  auto step = [&](auto KR, auto KN, Frag& cur, Frag& nxt, int64_t s) {
+    __builtin_amdgcn_s_waitcnt(kWait8);
+    asm volatile("s_barrier" ::: "memory");
+    issue(KR, s + 3 < nsteps);
+    read_frags(KN, nxt);
+    mfmas(cur);
+  };
+  for (int64_t s = 0; s < nsteps; s += 4) {
+    step(S3{}, S1{}, F0, F1, s);
+    if (s + 1 < nsteps) step(S0{}, S2{}, F1, F0, s + 1);
+    if (s + 2 < nsteps) step(S1{}, S3{}, F0, F1, s + 2);
+    if (s + 3 < nsteps) step(S2{}, S0{}, F1, F0, s + 3);
+  }
+  // no load into LDS may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue: lane holds rows 4*lgrp + v (M) of column (lane & 15) (N)
+  const int lgrp = lane >> 4;
+  const Rsrc ro = PART ? make_rsrc(p.out + ((bt * p.nsplit + split) * p.N * p.M) * 4,
+                                   static_cast<uint32_t>(p.N * p.M * 4))
+                       : make_rsrc(p.out + bt * p.o_batch * ES, static_cast<uint32_t>(p.N * p.ldo * ES));
+  const int64_t ldo = PART ? p.M : p.ldo;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * lgrp;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
+      const f32x4 v = acc[i][j];
+      if constexpr (PART) {
+        const uint32_t off = (n < p.N && m < p.M) ? static_cast<uint32_t>(n * ldo + m) * 4 : kOOB;
+        u32x4 w;
+        w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
+        w.z = __float_as_uint(v[2]); w.w = __float_as_uint(v[3]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
+      } else {
+        const uint32_t off = (n < p.N && m < p.M) ? static_cast<uint32_t>(n * ldo + m) * ES : kOOB;
+        u32x2 w;
+        w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
+        w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+      }
+    }
+  }
+}
+
 // out[bt][n][m] = sum_{s < nsplit} part[bt][s][n][m], summed in split order;
 // four consecutive m per thread (M % 4 == 0 on the split path).
 template <typename IO>
@@ -427,13 +669,20 @@ template <typename IO, bool VEC, bool PART>
 hipError_t launch_gemm_t(const GemmDev& p, hipStream_t st) {
   constexpr int BM = proj_bm<IO>(), BN = proj_bn<IO>();
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.nsplit * p.batch;
-  const size_t smem = proj_lds_bytes<IO>();
-  auto kern = ssm_proj_gemm_kernel<IO, VEC, PART>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(smem));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), smem, st, p);
-  return hipGetLastError();
+  if constexpr (VEC && std::is_same<IO, BF16>::value) {
+    // every size a multiple of 8, and lda = K and ldb = N in every
+    // contraction: each 16-byte chunk a DMA load fetches is whole and aligned
+    hipLaunchKernelGGL(ssm_proj_dma_kernel<PART>, dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), 0, st, p);
+    return hipGetLastError();
+  } else {
+    const size_t smem = proj_lds_bytes<IO>();
+    auto kern = ssm_proj_gemm_kernel<IO, VEC, PART>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), smem, st, p);
+    return hipGetLastError();
+  }
 }
 
 template <typename IO>

@@ -109,3 +109,27 @@ def test_no_scalar_cache_writes(all_isa):
     for src, text in all_isa.items():
         for op, args in _instructions(text):
             assert not bad.match(op), f"{src}: scalar-cache write {op} {args}"
+
+
+def test_lds_dma_m0_writes_and_waits(all_isa):
+    """The projection's bfloat16 kernel loads its operands straight into LDS
+    with inline-asm buffer loads whose LDS address is in M0.  In its
+    generated code: every such load is preceded by its own M0 write and one
+    wait state (s_nop), nothing else reads or writes M0, and the only full
+    vmcnt(0) wait is the drain before the workgroup ends (a compiler-inserted
+    wait inside the loop would serialize the pipeline)."""
+    text = all_isa["ssm_proj.hip"]
+    kernels = re.findall(r"^(_Z\w*ssm_proj_dma_kernel\w*):", text, flags=re.M)
+    assert kernels, "no DMA kernel in ssm_proj.hip"
+    for k in kernels:
+        body = text.split(k + ":", 1)[1].split("s_endpgm", 1)[0]
+        ins = _instructions(body)
+        loads = [i for i, (op, a) in enumerate(ins) if op.startswith("buffer_load") and a.rstrip().endswith("lds")]
+        assert loads, k
+        for i in loads:
+            assert ins[i - 1][0] == "s_nop", (k, ins[i - 1])
+            assert ins[i - 2][0] == "s_mov_b32" and ins[i - 2][1].startswith("m0,"), (k, ins[i - 2])
+        m0 = [i for i, (op, a) in enumerate(ins) if re.search(r"\bm0\b", a)]
+        assert set(m0) == {i - 2 for i in loads}, (k, [ins[i] for i in m0 if i + 2 not in loads])
+        full = [i for i, (op, a) in enumerate(ins) if op == "s_waitcnt" and "vmcnt(0)" in a]
+        assert len(full) == 1 and full[0] > max(loads), (k, len(full))
