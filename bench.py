@@ -115,10 +115,10 @@ MEASURED_AFFINE_TRAFFIC = {
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "ad29999056560c91", "fetch_bytes": 187093991, "write_bytes": 50339312,
+    "130m": {"digest": "bc782c669865d304", "fetch_bytes": 187230407, "write_bytes": 50341168,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
-    "1.4b": {"digest": "ad29999056560c91", "fetch_bytes": 404022732, "write_bytes": 83096608,
-             "profile": "profiles/ssm_proj_gemm_kernel_out_proj_1.4b_bf16.md"},
+    "1.4b": {"digest": "bc782c669865d304", "fetch_bytes": 402999173, "write_bytes": 70277240,
+             "profile": "profiles/ssm_proj_dma_kernel_out_proj_1.4b_bf16.md"},
 }
 
 

@@ -415,10 +415,12 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) 
 // bfloat16, every size a multiple of 8: the operands DMA'd into LDS.
 //
 // Stage layout (32 KB): A [256 m][32 k] in 64-byte rows whose 16-byte chunk
-// c sits at position c ^ ((m >> 2) & 3); B [32 k][256 n] in 512-byte rows
-// whose chunk c sits at c ^ swz_kn(k).  Both make the fragment reads spread
-// over every bank: 16 lanes reading one chunk of 16 consecutive A rows, and
-// one transposing read covering 16 B rows (k = 8 g + t, t < 4) x 32 bytes.
+// c sits at position c ^ ((m >> 1) & 3); B [32 k][256 n] in 512-byte rows
+// whose chunk c sits at c ^ swz_kn(k).  With 32 banks of 4 bytes, both keep
+// the fragment reads free of bank conflicts (counted: zero): any 8
+// consecutive lanes of an A read (one chunk of 8 consecutive rows) and any
+// 16 consecutive lanes of a transposing B read (4 k-rows x 32 bytes) cover
+// 128 distinct bytes of the bank space.
 // A DMA load writes 16 bytes per lane at block base + 16 lane, so the
 // swizzle is applied by choosing which global chunk each lane fetches.
 // --------------------------------------------------------------------------
@@ -494,7 +496,7 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   for (int i = 0; i < 4; ++i) {
     const int q = wave + 4 * i;
     const int ra = 16 * q + (lane >> 2);
-    const int ca = (lane & 3) ^ ((ra >> 2) & 3);
+    const int ca = (lane & 3) ^ ((ra >> 1) & 3);
     a_ok[i] = m0 + ra < p.M;
     a_k[i] = 8 * ca;
     a_off[i] = static_cast<uint32_t>((m0 + ra) * astride) + static_cast<uint32_t>(8 * ca * ES);
@@ -540,7 +542,7 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   // ---- fragments: A lane reads row wm*128 + 16 i + (lane & 15), chunk
   // lane >> 4 (k 8 (lane >> 4) ..); B lane 16 g + s reads k-row 8 g + s / 4
   // (+ 4 for k 8 g + 4 ..) at n = wn*128 + 16 j + 4 (s & 3)
-  const int a_lo = (wm * 128 + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ (((lane & 15) >> 2) & 3));
+  const int a_lo = (wm * 128 + (lane & 15)) * 64 + 16 * ((lane >> 4) ^ (((lane & 15) >> 1) & 3));
   const int kB = 8 * (lane >> 4) + ((lane & 15) >> 2);
   int b_lo[TJ];
 #pragma unroll
@@ -550,11 +552,13 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   struct Frag {
     uint4 a[TI], b[TJ];
   };
-  auto read_frags = [&](auto KS, Frag& f) {
+  auto read_a = [&](auto KS, Frag& f) {
     const char* sa = stg[decltype(KS)::value];
-    const char* sb = sa + kDmaA;
 #pragma unroll
     for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const uint4*>(sa + a_lo + 1024 * i);
+  };
+  auto read_b = [&](auto KS, Frag& f) {
+    const char* sb = stg[decltype(KS)::value] + kDmaA;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sb + b_lo[j]));
@@ -568,9 +572,9 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mfmas = [&](const Frag& f) {
+  auto mfma_rows = [&](const Frag& f, auto I0) {   // MFMA rows I0, I0 + 1
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = decltype(I0)::value; i < decltype(I0)::value + 2; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f.a[i]), as_bf16x8(f.b[j]), acc[i][j], 0, 0, 0);
@@ -579,28 +583,39 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   // ---- pipeline.  Step s: wait until stage s + 1 has landed (8 loads per
   // wave per stage, so vmcnt(8) leaves only stage s + 2 in flight) and until
   // this wave's reads issued at step s - 1 are done (lgkmcnt(0)); barrier
-  // (no fence: a release fence would wait for every load in flight); refill
-  // the stage read at step s - 1 with stage s + 3; read step s + 1's
-  // fragments; step s's MFMAs.
+  // (no fence: a release fence would wait for every load in flight); then
+  // step s's 64 MFMAs in four groups, with the refill of the stage read at
+  // step s - 1 (stage s + 3) and the reads of step s + 1's fragments issued
+  // between the groups.  (The inline-asm loads keep the compiler from
+  // moving the MFMAs across them, so this order is the issue order.)
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
   constexpr int kWait16 = 0 | (7 << 4) | (0 << 8) | (1 << 14);   // vmcnt(16) lgkmcnt(0)
   constexpr int kWait8 = 8 | (7 << 4) | (0 << 8);                // vmcnt(8) lgkmcnt(0)
+  using R0 = std::integral_constant<int, 0>;
+  using R2 = std::integral_constant<int, 2>;
+  using R4 = std::integral_constant<int, 4>;
+  using R6 = std::integral_constant<int, 6>;
   Frag F0, F1;
   issue(S0{}, 0 < nsteps);
   issue(S1{}, 1 < nsteps);
   issue(S2{}, 2 < nsteps);
   __builtin_amdgcn_s_waitcnt(kWait16);
   asm volatile("s_barrier" ::: "memory");
-  read_frags(S0{}, F0);
+  read_a(S0{}, F0);
+  read_b(S0{}, F0);
   auto step = [&](auto KR, auto KN, Frag& cur, Frag& nxt, int64_t s) {
     __builtin_amdgcn_s_waitcnt(kWait8);
     asm volatile("s_barrier" ::: "memory");
+    mfma_rows(cur, R0{});
     issue(KR, s + 3 < nsteps);
-    read_frags(KN, nxt);
-    mfmas(cur);
+    mfma_rows(cur, R2{});
+    read_a(KN, nxt);
+    mfma_rows(cur, R4{});
+    read_b(KN, nxt);
+    mfma_rows(cur, R6{});
   };
   for (int64_t s = 0; s < nsteps; s += 4) {
     step(S3{}, S1{}, F0, F1, s);
