@@ -510,32 +510,61 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
   const uint32_t bbytes = static_cast<uint32_t>(p.K * p.ldb * ES);
   const int64_t ksteps = (p.K + BK - 1) / BK;
   const int64_t nsteps = (seg1 - seg0) * ksteps;
-  // The stages are issued in order; (cur_seg, cur_k0) is the next one.  A
-  // stage past the end is still issued, all of it past the buffers (zeros),
-  // so that every step issues the same number of loads and one vmcnt value
-  // serves every wait.
+  // Per-lane offsets relative to the stage's k0, past the buffer for rows
+  // and columns outside the problem.
+  uint32_t a_v[4], b_v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a_v[i] = a_ok[i] ? a_off[i] : kOOB;
+    b_v[i] = b_ok[i] ? b_off[i] : kOOB;
+  }
+  // The stages are issued in order.  The scalar cursor holds the next
+  // stage's k0 and segment, and the byte address of A and B at that k0 with
+  // the bytes left from there: the descriptors advance by one stage with
+  // scalar adds, so a whole stage needs no per-lane address arithmetic.  A
+  // stage past the end is still issued with an empty buffer (every load
+  // reads zeros), so that every step issues the same number of loads and
+  // one vmcnt value serves every wait.
   int64_t cur_seg = seg0, cur_k0 = 0;
+  uint64_t a_addr = reinterpret_cast<uint64_t>(p.a + (bt * p.a_batch + seg0 * p.a_seg) * ES);
+  uint64_t b_addr = reinterpret_cast<uint64_t>(p.b + (bt * p.b_batch + seg0 * p.b_seg) * ES);
+  uint32_t a_rec = abytes, b_rec = bbytes;
   auto issue = [&](auto KS, bool live) {
-    const int64_t seg = live ? cur_seg : seg0, k0 = cur_k0;
+    const u32x4 ra = dma_desc(reinterpret_cast<const void*>(a_addr), live ? a_rec : 0u);
+    const u32x4 rb = dma_desc(reinterpret_cast<const void*>(b_addr), live ? b_rec : 0u);
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)stg[decltype(KS)::value]));
+    const int64_t left = p.K - cur_k0;
+    if (!live || left >= BK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave + 4 * i;
+        dma16(ra, a_v[i], base + q * 1024);
+        dma16(rb, b_v[i], base + kDmaA + q * 1024);
+      }
+    } else {
+      // the last stage of a segment with K % 32 != 0: k past K reads zeros
+      const int krem = static_cast<int>(left);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave + 4 * i;
+        dma16(ra, a_k[i] < krem ? a_v[i] : kOOB, base + q * 1024);
+        dma16(rb, b_k[i] < krem ? b_v[i] : kOOB, base + kDmaA + q * 1024);
+      }
+    }
     if (live) {
       cur_k0 += BK;
+      a_addr += static_cast<uint64_t>(BK * ES);
+      a_rec -= static_cast<uint32_t>(BK * ES);
+      b_addr += static_cast<uint64_t>(BK) * bstride;
+      b_rec -= static_cast<uint32_t>(BK) * bstride;
       if (cur_k0 >= ksteps * BK) {
         cur_k0 = 0;
         ++cur_seg;
+        a_addr = reinterpret_cast<uint64_t>(p.a + (bt * p.a_batch + cur_seg * p.a_seg) * ES);
+        b_addr = reinterpret_cast<uint64_t>(p.b + (bt * p.b_batch + cur_seg * p.b_seg) * ES);
+        a_rec = abytes;
+        b_rec = bbytes;
       }
-    }
-    const u32x4 ra = dma_desc(p.a + (bt * p.a_batch + seg * p.a_seg) * ES, abytes);
-    const u32x4 rb = dma_desc(p.b + (bt * p.b_batch + seg * p.b_seg) * ES, bbytes);
-    const int64_t left = p.K - k0;
-    const int krem = !live ? -1 : (left > BK ? BK : static_cast<int>(left));
-    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)stg[decltype(KS)::value]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave + 4 * i;
-      const bool oka = a_ok[i] & (a_k[i] < krem);
-      dma16(ra, oka ? a_off[i] + static_cast<uint32_t>(k0 * ES) : kOOB, base + q * 1024);
-      const bool okb = b_ok[i] & (b_k[i] < krem);
-      dma16(rb, okb ? b_off[i] + static_cast<uint32_t>(k0) * bstride : kOOB, base + kDmaA + q * 1024);
     }
   };
 
