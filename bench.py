@@ -115,9 +115,9 @@ MEASURED_AFFINE_TRAFFIC = {
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "bc782c669865d304", "fetch_bytes": 187230407, "write_bytes": 50341168,
+    "130m": {"digest": "0a6fb3443f0d4a3c", "fetch_bytes": 187281295, "write_bytes": 50341856,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
-    "1.4b": {"digest": "bc782c669865d304", "fetch_bytes": 402999173, "write_bytes": 70277240,
+    "1.4b": {"digest": "0a6fb3443f0d4a3c", "fetch_bytes": 403034661, "write_bytes": 70321720,
              "profile": "profiles/ssm_proj_dma_kernel_out_proj_1.4b_bf16.md"},
 }
 
