@@ -42,6 +42,14 @@ CASES = [
     (3, 40, 24, 1),           # one step
     (1, 1, 16, 40),           # d_inner = 1
     (1, 520, 260, 260),       # one past a tile in every dimension
+    # every size a multiple of 8: the bfloat16 path that loads straight into
+    # LDS, with a K tail shorter than its 32-value stage (forward K = d_inner,
+    # dy K = d_model, dW K = L) and ragged M and N tiles
+    (2, 200, 136, 304),
+    (3, 520, 264, 264),
+    (4, 320, 136, 200),
+    (1, 8, 8, 8),
+    (2, 1544, 776, 520),
 ]
 
 
