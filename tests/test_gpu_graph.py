@@ -1,6 +1,7 @@
 """The library's launches inside a captured HIP graph (torch.cuda.CUDAGraph):
 the decode step (the launch-bound path a serving loop would capture), the
-decode step with the conv in front, and the single-launch forward plans.
+decode step with the conv in front, the single-launch forward plans and the
+output projection's forward.
 
 Each graph is replayed several times with the program's own eager work
 (in-place updates of the inputs) and synchronizations between the replays,
@@ -124,4 +125,23 @@ def test_forward_replays_match_eager(plan):
         torch.cuda.synchronize(DEV)
         assert torch.equal(y_g, y_e) and torch.equal(last_g, last_e), f"replay {r}"
         inp["u"].mul_(-1.0)
+        torch.cuda.synchronize(DEV)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_out_proj_replays_match_eager(dtype):
+    """The output projection allocates nothing for its forward (bfloat16 with
+    every size a multiple of 8 takes the kernel that loads into LDS
+    directly): captured once, replayed with in-place updates of y between
+    replays, each replay equal to the eager launch bit for bit."""
+    inp = workloads.make_proj_inputs(2, 520, 264, 264, dtype=dtype, device=DEV, seed=17)
+    out_g = torch.empty((2, 264, 264), device=DEV, dtype=dtype)
+    graph = _capture(lambda: ssm.ssm_out_proj(inp["y"], inp["W"], out=out_g))
+    out_e = torch.empty_like(out_g)
+    for r in range(3):
+        graph.replay()
+        ssm.ssm_out_proj(inp["y"], inp["W"], out=out_e)
+        torch.cuda.synchronize(DEV)
+        assert torch.equal(out_g, out_e), f"replay {r}"
+        inp["y"].mul_(-0.5)
         torch.cuda.synchronize(DEV)
