@@ -835,11 +835,12 @@ def main():
     copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     plan = ssm.plan_for(w.batch, w.dim, w.dstate, w.L, w.dtype)
-    if args.plan != "auto":
-        plan["plan"] = args.plan
+    if args.plan != "auto" or args.states_per_lane or args.chunk:
+        # an explicit plan: report what was asked for (0: left to the library)
+        plan = {"plan": args.plan, "states_per_lane": args.states_per_lane, "chunk": args.chunk, "explicit": True}
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
     key = w.name + (f"+conv{args.conv}" if args.conv else "")
-    traffic = None if (use_states or args.conv_u_out) else measured_traffic(key, plan)
+    traffic = None if (use_states or args.conv_u_out or plan.get("explicit")) else measured_traffic(key, plan)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
