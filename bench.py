@@ -13,14 +13,21 @@ Reported:
                = every input element once + y + last_state (no (a,b) pairs,
                no per-step states).
   hbm_frac     value / 8000 GB/s (MI355X HBM3E peak).
-  roofline     the binding roof of the scan kernel.  The recurrence costs, per
-               (channel, state, step), one v_exp_f32 (half rate on gfx950,
+  roofline     the HBM roof: value against 8000 GB/s, with the measured HBM
+               traffic per launch where a counter profile of the same kernel
+               build is stored.
+  alu_roofline the floor of the recurrence's own arithmetic.  Per (channel,
+               state, step) it costs one v_exp_f32 (half rate on gfx950,
                measured) plus two v_mul and two v_fma: 6 VALU issue slots.
                MI355X issues 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz =
                39.32e12 lane-slots/s without packed-FP32 instructions, so the
                mix peaks at 39.32e12 / 6 state-steps/s; counting the mix as 7
                FLOP (mul 1, exp 1, mul 1, fma 2, fma 2) that is 45.9 TFLOP/s.
-  cpu_baseline the float64 C oracle (OpenMP over channels) on the host cores.
+  prewarm      seconds of untimed launches after the W warm-up steps, so
+               the timed steps run at the settled shader clock.
+  cpu_baseline the float64 C oracle (OpenMP over channels) on the host cores,
+               with the CPU model.
+  context      the pages' own single-A100 anecdotes (not a target).
 """
 from __future__ import annotations
 
@@ -39,6 +46,51 @@ LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9          # non-packed FP32 VALU issue
 SLOTS_PER_STATE_STEP = 6.0                      # exp (2 slots) + 2 mul + 2 fma
 FLOP_PER_STATE_STEP = 7.0
 ALU_PEAK_TFLOPS = LANE_SLOTS_PER_S / SLOTS_PER_STATE_STEP * FLOP_PER_STATE_STEP / 1e12
+
+
+# The pages' own numbers for this path, all from one A100 and quoted as
+# context only (another machine, not a target): the fused scan kernel
+# against a conv1d formulation at L = 2048, and the bandwidth the scan was
+# seen to reach in deployment ("The hardware truth of Mamba's parallel scan",
+# sections 1 and 3).
+PAGES_CONTEXT = {
+    "note": "context only, not a target: single-A100 anecdotes from the Truth page "
+            "('The hardware truth of Mamba's parallel scan')",
+    "a100_tokens_per_s_conv1d_vs_fused_L2048": [85, 327],
+    "a100_scan_bandwidth_gbs_observed_of_peak": [820, 2039],
+}
+
+PREWARM_S = 0.5   # seconds of the same launches before the timed region
+
+
+def prewarm(step, dev, seconds=PREWARM_S):
+    """Run ``step`` back to back for at least ``seconds`` of wall time, so the
+    GPU sits at its steady clock when the timed region starts (the scan
+    kernels are bound by their instruction issue, so their time follows the
+    shader clock, which takes on the order of 0.1 s of load to settle).
+    Returns (seconds spent, launches)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize(dev)
+        if time.perf_counter() - t0 >= seconds:
+            return time.perf_counter() - t0, n
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -244,6 +296,7 @@ def decode_bench(args):
         for _ in range(max(1, args.warmup // per_run)):
             run()
         torch.cuda.synchronize(dev)
+    prewarm(run, dev)
     nrun = max(1, args.steps // per_run)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -298,7 +351,7 @@ def decode_bench(args):
                 break
             rows = min(4 * rows, w.batch)
         res["cpu_baseline"] = {"value": round(bytes_alg * rows / w.batch / spent / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"{rows} of {w.batch} sequences, one step (float64 NumPy, elementwise "
                                          "operations on one thread)"}
     print(json.dumps(res), flush=True)
@@ -375,7 +428,7 @@ def bwd_cpu_baseline(inp, gr, w, budget_s):
     elapsed = run(nb, nd)
     frac = nb * nd / (w.batch * w.dim)
     gbs = bwd_algorithmic_bytes(w, 128) * frac / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{nb} of {w.batch} batch rows x {nd} of {w.dim} channels x {w.L} steps x {w.dstate} states "
                       f"({elapsed:.1f} s, float64 C gradient oracle, OpenMP static over channels)",
             "gsteps_ch_state_per_s": round(w.state_steps() * frac / elapsed / 1e9, 4)}
@@ -421,6 +474,7 @@ def bwd_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
+    prewarm(step, dev)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -505,6 +559,7 @@ def affine_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
+    prewarm(step, dev)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -538,7 +593,7 @@ def affine_bench(args):
                 break
             nr = min(4 * nr, rows)
         res["cpu_baseline"] = {"value": round(16 * nr * L / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"{nr} of {rows} rows x {L} steps (float64 NumPy serial fold, "
                                          "elementwise operations on one thread)"}
     print(json.dumps(res), flush=True)
@@ -580,6 +635,7 @@ def proj_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
+    prewarm(step, dev)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -630,7 +686,7 @@ def proj_bench(args):
             n *= 4
         res["cpu_baseline"] = {"value": round(2.0 * n * dm * w.dim / spent / 1e12, 6), "unit": "TFLOP/s",
                                "cores": blas_threads(),
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"{n} tokens x {dm} outputs (float64 NumPy matrix product)"}
     if args.cpu_seconds > 0 and args.bwd:
         # the gradient oracle on the first Ls tokens of one batch row (dy of
@@ -648,7 +704,7 @@ def proj_bench(args):
                 break
             ls = min(4 * ls, w.L)
         res["cpu_baseline"] = {"value": round(4.0 * ls * dm * w.dim / spent / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": blas_threads(), "kind": "oracle",
+                               "cores": blas_threads(), "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"{ls} tokens of one batch row: dy and dW terms (float64 NumPy)"}
     print(json.dumps(res), flush=True)
 
@@ -695,7 +751,7 @@ def cpu_baseline(inp, w, budget_s, threads=0):
         per_pass = run(nrows, passes)
     frac = nrows / rows_total
     gbs = w.algorithmic_bytes() * frac / per_pass / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{nrows} of {rows_total} channels x {w.L} steps x {w.dstate} states, {passes} pass(es) "
                       f"({per_pass * passes:.1f} s, float64 C recurrence, OpenMP static over channels)",
             "gsteps_ch_state_per_s": round(w.state_steps() * frac / per_pass / 1e9, 4)}
@@ -782,6 +838,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    prewarm_s, prewarm_n = prewarm(step, dev)
     # One event pair on the launch stream around the K back-to-back steps
     # (torch's current stream, which the binding passes to the library): the
     # average is the kernel time per step plus the small gap between
@@ -862,14 +919,18 @@ def main():
                    **({"state_chunk": args.state_chunk} if args.state_chunk else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
-                     "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4), "traffic": traffic},
-        "hbm_roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                         "algorithmic_bytes": bytes_alg},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes": bytes_alg},
+        "alu_roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
+                         "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
+                         "note": "floor of the recurrence's own instruction mix: 6 VALU issue slots per "
+                                 "state-step at 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz"},
+        "prewarm": {"seconds": round(prewarm_s, 3), "launches": prewarm_n,
+                    "note": "untimed launches after the warm-up so the shader clock has settled"},
         "cold": {"ms_per_step": round(ms_cold, 5), "value": round(bytes_alg / (ms_cold * 1e-3) / 1e9, 2),
                  "unit": "GB/s", "note": "median of 20 single launches, each after a 512 MiB write"},
         "hbm_copy_gbs": round(copy_gbs, 1),
+        "context": PAGES_CONTEXT,
     }
     if w.dtype == "bf16":
         out["dtype"] = "f32 (bf16 storage)"

@@ -245,15 +245,28 @@ __device__ __forceinline__ float get(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
-// Delta in log2 units from raw delta: x2 = (delta + bias) * log2(e);
-// softplus(x) * log2(e) = log2(1 + 2^x2) ([Scan page] §1.2 softplus), taken
-// as x2 itself above 64 where 2^-x2 is below float32 resolution.  The
-// compare-and-select form keeps NaN inputs NaN and maps -inf to exactly 0.
+// softplus in log2 units: log2(1 + 2^x2) = max(x2, 0) + log2(1 + e) with
+// e = 2^-|x2| in (0, 1] ([Scan page] §1.2: Delta is made positive with
+// softplus).  w = 1 + e is rounded; c = e - (w - 1) is that rounding error
+// exactly (w - 1 is exact for w in [1, 2], and e and w - 1 are within a
+// factor of two of each other or w - 1 is 0), and log2(1 + e) =
+// log2(w) + c / (w ln 2) + O(c^2).  Taking c / w as c leaves an error below
+// 2^-24 of the result, so the value keeps float32 relative precision as
+// 2^x2 -> 0, where log2(1 + 2^x2) alone rounds to 0 (x2 below about -24,
+// i.e. delta + bias below about -16.6) and loses digits well before.
+// NaN stays NaN; -inf gives exactly 0 and +inf gives +inf.
+__device__ __forceinline__ float softplus2(float x2) {
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x2));
+  const float w = 1.0f + e;
+  const float c = e - (w - 1.0f);
+  return __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(w)) + __builtin_fmaxf(x2, 0.0f);
+}
+
+// Delta in log2 units from raw delta: x2 = (delta + bias) * log2(e), and
+// softplus(x) * log2(e) = softplus2(x2).
 __device__ __forceinline__ float delta2(float dl, float bias2, bool softplus) {
   const float x2 = __builtin_fmaf(dl, kLog2e, bias2);
-  if (!softplus) return x2;
-  const float sp = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x2));
-  return x2 > 64.0f ? x2 : sp;
+  return softplus ? softplus2(x2) : x2;
 }
 
 // silu(z) = z / (1 + e^-z) ([Mamba-2 page] §4.1 SiLU gate).

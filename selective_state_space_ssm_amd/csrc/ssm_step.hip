@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm_device.h"
 #include "ssm_kernels.h"
 
 namespace ssm {
@@ -172,15 +173,12 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   } else {
     uu = IO::ld(a.u + chc);
   }
-  float dt = x;
-  if (a.softplus) {
-    // softplus(x) = log(1 + e^x), computed as ln2 * log2(1 + 2^(x log2 e));
-    // x itself above 44 (where e^-x is below float32 resolution)
-    const float sp = 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e));
-    dt = x > 44.0f ? x : sp;
-  }
+  // Delta in log2 units (dt2) and in natural units (dt): softplus(x) =
+  // ln2 * softplus2(x log2 e), accurate as e^x -> 0
+  const float x2 = x * kLog2e;
+  const float dt2 = a.softplus ? dev::softplus2(x2) : x2;
+  const float dt = a.softplus ? dt2 * dev::kLn2 : x;
   const float dtu = dt * uu;
-  const float dt2 = dt * kLog2e;
 
   float part = 0.0f;
   if (has_states) {

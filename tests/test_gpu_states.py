@@ -111,10 +111,11 @@ def test_split_runs_compose(plan):
 
 
 @pytest.mark.parametrize("name,sc", [("130m", 256), ("long", 4096)])
-def test_full_size_sampled(name, sc):
+def test_full_size(name, sc):
     """Full-size workload with a random start state and chunk states, in the
-    automatic launch configuration, on sampled whole channels."""
-    from oracle import cpu
+    automatic launch configuration: every element of y, last_state and the
+    chunk states against the C oracle."""
+    import fullcheck
     w = workloads.WORKLOADS[name]
     print(f"[states full-size] {name}: b={w.batch} d={w.dim} L={w.L} state_chunk={sc}", flush=True)
     inp = workloads.make_inputs(w, device=DEV, seed=0)
@@ -125,18 +126,8 @@ def test_full_size_sampled(name, sc):
                                           inp["delta_bias"], delta_softplus=w.softplus, h0=inp["h0"],
                                           state_chunk=sc)
     torch.cuda.synchronize(DEV)
-    rng = np.random.default_rng(3)
-    rb = rng.integers(0, w.batch, 48)
-    rd = rng.integers(0, w.dim, 48)
-    tb, td = torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV)
-    sel = lambda x: None if x is None else x[tb, td].float().cpu().numpy()
-    y_ref, last_ref, bnd_ref = cpu.fwd_rows(sel(inp["u"]), sel(inp["delta"]), sel(inp["z"]), rb, rd,
-                                            _host(inp["A"]), _host(inp["B"]), _host(inp["C"]), _host(inp["D"]),
-                                            _host(inp["delta_bias"]), w.softplus, w.batch, w.dim, w.dstate, w.L,
-                                            h0_rows=sel(inp["h0"]), chunk=sc)
+    err = fullcheck.compare_forward(inp, y, last, h0=inp["h0"], chunk_states=cs, state_chunk=sc)
     tol = TOL[w.torch_dtype]
-    ey = rel_err(_host(y[tb, td]), y_ref)
-    eh = rel_err(_host(last[tb, td]), last_ref)
-    ec = rel_err(_host(cs[tb, :, td]), bnd_ref)
-    print(f"[states full-size] {name}: y {ey:.3e} last {eh:.3e} chunk states {ec:.3e}", flush=True)
-    assert ey <= tol and eh <= 1e-4 and ec <= 1e-4
+    print(f"[states full-size] {name}: y {err['y']:.3e} last {err['last_state']:.3e} "
+          f"chunk states {err['chunk_states']:.3e}", flush=True)
+    assert err["y"] <= tol and err["last_state"] <= 1e-4 and err["chunk_states"] <= 1e-4
