@@ -69,6 +69,8 @@ def prewarm(step, dev, seconds=PREWARM_S):
     kernels are bound by their instruction issue, so their time follows the
     shader clock, which takes on the order of 0.1 s of load to settle).
     Returns (seconds spent, launches)."""
+    if seconds <= 0:
+        return 0.0, 0
     import torch
     t0 = time.perf_counter()
     n = 0
@@ -100,6 +102,8 @@ def parse():
     # a few hundred untimed steps (~0.1 s) let the GPU reach its steady clock
     p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--workload", default="130m")
+    p.add_argument("--prewarm", type=float, default=PREWARM_S,
+                   help="seconds of untimed launches after the warm-up steps (0: none, for counter runs)")
     p.add_argument("--plan", default="auto")
     p.add_argument("--states-per-lane", type=int, default=0)
     p.add_argument("--chunk", type=int, default=0)
@@ -296,7 +300,7 @@ def decode_bench(args):
         for _ in range(max(1, args.warmup // per_run)):
             run()
         torch.cuda.synchronize(dev)
-    prewarm(run, dev)
+    prewarm(run, dev, args.prewarm)
     nrun = max(1, args.steps // per_run)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -474,7 +478,7 @@ def bwd_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev)
+    prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -559,7 +563,7 @@ def affine_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev)
+    prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -635,7 +639,7 @@ def proj_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev)
+    prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -838,7 +842,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    prewarm_s, prewarm_n = prewarm(step, dev)
+    prewarm_s, prewarm_n = prewarm(step, dev, args.prewarm)
     # One event pair on the launch stream around the K back-to-back steps
     # (torch's current stream, which the binding passes to the library): the
     # average is the kernel time per step plus the small gap between
