@@ -101,6 +101,33 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
                  int dtype, void *stream);
 
 /*
+ * ssm_scan_fwd_noalloc -- ssm_scan_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It calls no hipMalloc, hipFree,
+ * hipMallocAsync or other allocating routine: the two-pass plan's workspace
+ * (chunk aggregates and chunk start states, 12 * batch * d_inner * d_state
+ * * K bytes for K chunks) lives in a fixed per-device scratch array of
+ * 8 MiB (8388608 bytes) that the library holds on every GPU it runs on
+ * until the process ends.  Its device address is looked up once per device,
+ * on the first call with that device current.
+ *   Arguments, semantics and results: as ssm_scan_fwd (the same plan, the
+ *   same kernels, bit for bit the same outputs).
+ *   Errors: as ssm_scan_fwd, plus SSM_EUNSUPPORTED when the plan's
+ *   workspace would exceed the scratch (never for the automatic plan, whose
+ *   two-pass split stays below 7.1 MB), and SSM_EHIP if the scratch's
+ *   address cannot be looked up.
+ *   Concurrency: every call on one GPU uses that GPU's one scratch array;
+ *   calls whose work overlaps on one GPU (other streams, other host
+ *   threads) race on it.  Calls ordered on one stream do not.  Each call
+ *   writes every word of the scratch it reads, so nothing needs clearing.
+ */
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                         const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                         void *y, float *last_state,
+                         int64_t batch, int64_t d_inner, int64_t d_state, int64_t L,
+                         int dtype, void *stream);
+
+/*
  * ssm_scan_fwd_plan -- ssm_scan_fwd with an explicit plan
  * ([Scan page] §2.2 and §3.3 describe both decompositions).
  *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY, SSM_PLAN_TWOPASS or

@@ -56,6 +56,8 @@ def load_library():
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
     lib.ssm_scan_fwd.restype = I
+    lib.ssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
+    lib.ssm_scan_fwd_noalloc.restype = I
     lib.ssm_scan_fwd_plan.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, I, I, I64, P]
     lib.ssm_scan_fwd_plan.restype = I
     lib.ssm_scan_fwd_states.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
@@ -166,6 +168,52 @@ def ssm_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                                    _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
                                    bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16,
                                    PLANS[plan], int(states_per_lane), int(chunk), _stream(device))
+    _check(rc)
+    return y, last_state
+
+
+def ssm_scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                         delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                         y: Optional[torch.Tensor] = None,
+                         last_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``ssm_scan_fwd`` through the entry point that allocates no device
+    memory (see ``ssm_scan_fwd_noalloc`` in include/ssm_scan.h): the library
+    call itself allocates nothing; pass ``y`` (and ``last_state``) to keep
+    this wrapper from allocating them with torch.  Calls that overlap on one
+    GPU race on its fixed scratch."""
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError("ssm_scan_fwd_noalloc needs CUDA/HIP tensors")
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [b, d, L] and A [d, n]")
+    bsz, dim, L = u.shape
+    n = A.shape[1]
+    dt = u.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("u must be float32 or bfloat16")
+    _need(u, "u", dt, device, (bsz, dim, L))
+    _need(delta, "delta", dt, device, (bsz, dim, L))
+    _need(A, "A", torch.float32, device, (dim, n))
+    _need(B, "B", dt, device, (bsz, n, L))
+    _need(C, "C", dt, device, (bsz, n, L))
+    if z is not None:
+        _need(z, "z", dt, device, (bsz, dim, L))
+    if D is not None:
+        _need(D, "D", torch.float32, device, (dim,))
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", torch.float32, device, (dim,))
+    if y is None:
+        y = torch.empty_like(u)
+    else:
+        _need(y, "y", dt, device, (bsz, dim, L))
+    if last_state is not None:
+        _need(last_state, "last_state", torch.float32, device, (bsz, dim, n))
+    lib = load_library()
+    with torch.cuda.device(device):
+        rc = lib.ssm_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+                                      bsz, dim, n, L, SSM_F32 if dt == torch.float32 else SSM_BF16, _stream(device))
     _check(rc)
     return y, last_state
 

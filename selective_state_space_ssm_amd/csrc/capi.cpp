@@ -128,11 +128,19 @@ int check_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t L) {
   return SSM_OK;
 }
 
+// Where the two-pass workspace comes from: nullptr = stream-ordered
+// allocation per call; otherwise a fixed region of `bytes` whose device
+// address `get` returns (called only after every argument has been checked).
+struct FixedWorkspace {
+  size_t bytes;
+  hipError_t (*get)(void** ptr);
+};
+
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int delta_softplus, const float* h0, void* y,
                   float* last_state, float* chunk_states, int64_t state_chunk, int64_t batch, int64_t dim,
                   int64_t dstate, int64_t L, int dtype, int plan, int S_req, int64_t chunk_req, const float* conv_w, const float* conv_b,
-                  int conv_k, void* u_out, void* stream) {
+                  int conv_k, void* u_out, void* stream, const FixedWorkspace* fixed_ws = nullptr) {
   g_err.clear();
   if (!u || !delta || !A || !B || !C || !y)
     return fail(SSM_EINVAL, "u, delta, A, B, C and y must not be NULL");
@@ -219,9 +227,19 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   const int64_t rows = batch * dstate * dim;
   const size_t per = sizeof(float) * static_cast<size_t>(rows) * static_cast<size_t>(K);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, 3 * per, st);
-  if (e == hipErrorOutOfMemory) return fail(SSM_ENOMEM, "two-pass workspace of %zu bytes", 3 * per);
-  if (e != hipSuccess) return hip_fail(e, "two-pass workspace allocation");
+  hipError_t e;
+  if (fixed_ws != nullptr) {
+    if (3 * per > fixed_ws->bytes)
+      return fail(SSM_EUNSUPPORTED,
+                  "the two-pass workspace of %zu bytes (%lld chunks) exceeds the %zu-byte scratch of the "
+                  "no-allocation entry point", 3 * per, (long long)K, fixed_ws->bytes);
+    e = fixed_ws->get(&ws);
+    if (e != hipSuccess) return hip_fail(e, "no-allocation scratch lookup");
+  } else {
+    e = hipMallocAsync(&ws, 3 * per, st);
+    if (e == hipErrorOutOfMemory) return fail(SSM_ENOMEM, "two-pass workspace of %zu bytes", 3 * per);
+    if (e != hipSuccess) return hip_fail(e, "two-pass workspace allocation");
+  }
   float* agg_p = static_cast<float*>(ws);
   float* agg_h = agg_p + rows * K;
   float* h_init = agg_h + rows * K;
@@ -236,7 +254,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
     a.h_init = h_init;
     e = ssm::launch_rows_full(a, bf16, S, K, st);
   }
-  hipError_t ef = hipFreeAsync(ws, st);
+  hipError_t ef = fixed_ws != nullptr ? hipSuccess : hipFreeAsync(ws, st);
   if (e != hipSuccess) return hip_fail(e, "two-pass launch");
   if (ef != hipSuccess) return hip_fail(ef, "two-pass workspace release");
   return SSM_OK;
@@ -251,6 +269,16 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype, void* stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
                        d_inner, d_state, L, dtype, SSM_PLAN_AUTO, 0, 0, nullptr, nullptr, 0, nullptr, stream);
+}
+
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                         float* last_state, int64_t batch, int64_t d_inner, int64_t d_state, int64_t L, int dtype,
+                         void* stream) {
+  static const FixedWorkspace scratch{ssm::kNoAllocScratchBytes, &ssm::noalloc_scratch};
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, y, last_state, nullptr, 0, batch,
+                       d_inner, d_state, L, dtype, SSM_PLAN_AUTO, 0, 0, nullptr, nullptr, 0, nullptr, stream,
+                       &scratch);
 }
 
 int ssm_scan_fwd_plan(const void* u, const void* delta, const float* A, const void* B, const void* C,

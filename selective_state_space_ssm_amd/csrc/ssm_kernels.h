@@ -121,6 +121,12 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, int S, hipStream_t st);
 // Fill n floats with zero (a kernel, not a memset).
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 
+// Fixed per-device scratch of the entry point that allocates nothing
+// (noalloc.hip): its size in bytes, and its device address on the current
+// device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // affine_scan association-order constants and launcher
 constexpr int kAffT = 8;      // items per lane
 constexpr int kAffLanes = 64; // lanes per wave

@@ -265,3 +265,38 @@ def test_out_proj_bwd_rejects_bad_arguments():
     assert call(dw=P(BIG + 256)) == ssm.SSM_EINVAL                     # dW inside y
     assert call(dw=P(4 * BIG + 64)) == ssm.SSM_EINVAL                  # dW inside dy
     assert call(m=1 << 16, k=1 << 14) == ssm.SSM_EUNSUPPORTED          # W in float32 reaches 2^32 bytes
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call():
+    """The entry point that allocates nothing validates like ssm_scan_fwd."""
+    lib = ssm.load_library()
+    P = ctypes.c_void_p
+    cases = [  # (u, y, batch, n, code)
+        (None, 8 * BIG, 1, 16, ssm.SSM_EINVAL),
+        (BIG, None, 1, 16, ssm.SSM_EINVAL),
+        (BIG, 8 * BIG, 0, 16, ssm.SSM_EINVAL),
+        (BIG, 8 * BIG, 1, 17, ssm.SSM_EUNSUPPORTED),
+        (BIG + 4, 8 * BIG, 1, 16, ssm.SSM_EINVAL),
+        (BIG, BIG, 1, 16, ssm.SSM_EINVAL),          # y overlaps u
+    ]
+    for u, y, b, n, code in cases:
+        rc = lib.ssm_scan_fwd_noalloc(P(u), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, None, None, 1,
+                                      P(y), None, b, 64, n, 4096, 0, None)
+        assert rc == code, (u, y, b, n, lib.ssm_last_error().decode())
+
+
+@pytest.mark.parametrize("L", [2048, 4096, 65536, 1 << 20, 1 << 22, ((1 << 32) - 4096) // 64])
+def test_automatic_two_pass_workspace_fits_the_noalloc_scratch(L):
+    """Wherever the automatic plan splits L (fewer channel groups than CUs),
+    its workspace, 3 float32 per (batch, channel, state, chunk), stays below
+    the 8 MiB scratch of ssm_scan_fwd_noalloc."""
+    worst = 0
+    for b in (1, 2, 3, 8, 16, 255):
+        for d in (1, 16, 17, 100, 255, 1024, 4080):
+            for n in (1, 16):
+                p = ssm.plan_for(b, d, n, L, "f32")
+                if p["plan"] != "twopass":
+                    continue
+                K = -(-L // p["chunk"])
+                worst = max(worst, 12 * b * d * n * K)
+    assert worst <= 8 << 20, worst
