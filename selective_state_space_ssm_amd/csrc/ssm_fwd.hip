@@ -140,7 +140,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 
   float* sDt = smem;                  // [16][kRow]  Delta2
   float* sDu = sDt + kCG * kRow;      // [16][kRow]  Delta * u
-  float* sBC = sDu + kCG * kRow;      // [2][16][kTT] B rows, then C rows (float32)
+  float* sBC = sDu + kCG * kRow;      // [2][16][kTT] B rows, then C rows (float32), swizzled (bc_col)
   float* sP = sBC + 2 * kNS * kTT;    // [NG][16][kRow] partial y (kFull only)
 
   const int lane = tid & 63;
@@ -314,6 +314,17 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     }
   };
 
+  // LDS position of B/C float4 group q (state n = (q / 8) % 16, steps
+  // 4 (q % 8) .. + 3, B for q < 128 and C after): the two 16-step halves of
+  // a state's row are swapped for states of odd lane rows (row group n / S
+  // odd), so that the two rows of 16 lanes that a 32-lane half of a wave
+  // reads in one LDS access land in different banks (32 banks of 4 bytes).
+  auto bc_slot = [&](int q) {
+    const int n = (q / (kTT / 4)) % kNS;
+    const int t = (q % (kTT / 4)) * 4;
+    return (q / (kTT / 4)) * kTT + (t ^ (16 * ((n / S) & 1)));
+  };
+
   // D*u and silu(z) of the tile just prepared (n*) and of the tile whose
   // epilogue is pending (c*).  Prep computes them from the loaded registers,
   // so no loaded value is ever copied: a copy would let the compiler keep the
@@ -392,7 +403,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       F32::template st<V>(sDt + pc * kRow + pt, dt);
       F32::template st<V>(sDu + pc * kRow + pt, du);
 #pragma unroll
-      for (int i = 0; i < BCQ; ++i) *reinterpret_cast<float4*>(sBC + (tid + i * NT) * 4) = rbc[i];
+      for (int i = 0; i < BCQ; ++i) *reinterpret_cast<float4*>(sBC + bc_slot(tid + i * NT)) = rbc[i];
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -416,7 +427,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
         v.y = t + 1 < t_end ? v.y : 0.0f;
         v.z = t + 2 < t_end ? v.z : 0.0f;
         v.w = t + 3 < t_end ? v.w : 0.0f;
-        *reinterpret_cast<float4*>(sBC + q * 4) = v;
+        *reinterpret_cast<float4*>(sBC + bc_slot(q)) = v;
       }
     }
   };
@@ -432,8 +443,9 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int n = grp * S + s;
-        bc[s][hh] = sBC[n * kTT + 16 * hh + col];
-        cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + 16 * hh + col] : 0.0f;
+        const int tt = (16 * hh) ^ (16 * (grp & 1));
+        bc[s][hh] = sBC[n * kTT + tt + col];
+        cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + tt + col] : 0.0f;
       }
     static_for<0, 2>([&](auto HH) {
       constexpr int hh = decltype(HH)::value;
