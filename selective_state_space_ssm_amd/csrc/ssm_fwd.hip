@@ -492,7 +492,24 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   };
 
   // ---- epilogue of the tile at t0: sum partials, D skip, gate, store
-  auto epilogue = [&](int t0) {
+  // bfloat16 vector stores of two tiles at once (see the epilogue)
+  constexpr bool kPairStores = std::is_same<IO, BF16>::value && VEC && V >= 2;
+  uint32_t yhold[kPairStores ? V / 2 : 1];
+  auto store_words = [&](uint32_t off, const uint32_t* w) {
+    if constexpr (V == 2) {
+      __builtin_amdgcn_raw_buffer_store_b32(w[0], rY, off, 0, 0);
+    } else if constexpr (V == 4) {
+      u32x2 x;
+      x.x = w[0]; x.y = w[1];
+      __builtin_amdgcn_raw_buffer_store_b64(x, rY, off, 0, 0);
+    } else {
+      u32x4 x;
+      x.x = w[0]; x.y = w[1]; x.z = w[2]; x.w = w[3];
+      __builtin_amdgcn_raw_buffer_store_b128(x, rY, off, 0, 0);
+    }
+  };
+  auto epilogue = [&](int t0, auto PARC) {
+    constexpr int PAR = decltype(PARC)::value;  // tile parity within the unrolled pair
     float acc[V];
     F32::template ld<V>(sP + pc * kRow + pt, acc);
 #pragma unroll
@@ -506,6 +523,18 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 #pragma unroll
     for (int e = 0; e < V; ++e) out[e] = kGate ? (acc[e] + cDu[e]) * cG[e] : acc[e] + cDu[e];
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if constexpr (kPairStores) {
+      // bfloat16: a tile's row slice is 64 bytes, half of a 128-byte line.
+      // The first tile of a pair keeps its packed outputs in registers and
+      // the second stores both halves back to back, so each line reaches
+      // the L2 whole rather than as two halves a tile apart.
+      if (PAR == 0 && t0 + kTT <= t_end) {
+#pragma unroll
+        for (int e = 0; e < V / 2; ++e) yhold[e] = BF16::cvt(out[2 * e]) | (BF16::cvt(out[2 * e + 1]) << 16);
+        return;
+      }
+      if (PAR == 1 && t0 <= t_end) store_words(poff + toff - kTT * ES, yhold);
+    }
     if (VEC && t0 + kTT <= t_end) {
       Buf::template st<V>(rY, poff + toff, out);
     } else {
@@ -555,7 +584,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       if (n < N) chunk_states[((b * nsc + kc) * dim + d) * N + n] = h[s];
     }
   };
-  auto half_step = [&](int t0, TileRegs& next, TileRegs& reload) {
+  auto half_step = [&](int t0, TileRegs& next, TileRegs& reload, auto PARC) {
     // With two or more states per lane the recurrence is a long VALU stream
     // while the other waves of the SIMD sit in the latency-bound prep and
     // epilogue: raising this wave's issue priority for the recurrence keeps
@@ -567,7 +596,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     save_states(t0);
     __syncthreads();
     prep(next);
-    if (MODE == kFull) epilogue(t0);
+    if (MODE == kFull) epilogue(t0, PARC);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       cDu[e] = nDu[e];
@@ -579,8 +608,8 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 #pragma unroll 1
   for (int it = 0; it < ntiles; it += 2) {
     const int t0 = t_begin + it * kTT;
-    half_step(t0, B, B);
-    half_step(t0 + kTT, A, A);
+    half_step(t0, B, B, std::integral_constant<int, 0>{});
+    half_step(t0 + kTT, A, A, std::integral_constant<int, 1>{});
   }
 
   // ---- chunk end: final state or chunk aggregate
@@ -618,8 +647,18 @@ __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(RowArgs<IO> args, 
   const int tid = threadIdx.x;
   // the wave index as an SGPR keeps every per-wave quantity uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  rows_group<IO, S, MODE, GATED, VEC, CONV>(args, p, smem, tid, wave, static_cast<int64_t>(blockIdx.x) * kCG,
-                                            blockIdx.y, blockIdx.z);
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its
+  // own L2.  The (group, batch row, chunk) order is remapped so that each
+  // XCD takes a contiguous range of it, channel groups fastest: an XCD then
+  // works on a few batch rows (or chunks) at a time, whose B and C stay in
+  // its L2 for all of their channel groups.
+  const int64_t X = gridDim.x, Y = gridDim.y;
+  const int64_t G = X * Y * gridDim.z;
+  const int64_t pid = blockIdx.x + X * (blockIdx.y + Y * static_cast<int64_t>(blockIdx.z));
+  const int64_t q = G / 8, r = G % 8, xcd = pid % 8, slot = pid / 8;
+  const int64_t logical = xcd * q + (xcd < r ? xcd : r) + slot;
+  rows_group<IO, S, MODE, GATED, VEC, CONV>(args, p, smem, tid, wave, (logical % X) * kCG, (logical / X) % Y,
+                                            logical / (X * Y));
 }
 
 struct MixedSizes {
@@ -669,6 +708,56 @@ __global__ __launch_bounds__(256) void ssm_combine_kernel(const float* __restric
   const int64_t b = i / (dim * dstate);
   float hv = h0 != nullptr ? h0[(b * dim + d) * dstate + n] : 0.0f;
   for (int64_t k = 0; k < K; ++k) {
+    h_init[k * rows + i] = hv;
+    if (k + 1 < K) hv = __builtin_fmaf(agg_p[k * rows + i], hv, agg_h[k * rows + i]);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Chunk combine for many chunks: the scan over the K chunk totals of
+// [Scan page] §3.3 as a blocked scan.  A workgroup takes 64 consecutive
+// rows (b, n, d); its 16 wavefronts split K into 16 segments (lane = row,
+// so every access is coalesced).  Each lane folds its segment's totals
+// (P, H) in chunk order, the segment totals meet in LDS and each lane
+// composes h0 with the totals of the segments before its own, in segment
+// order, then walks its segment again writing h_init^(k).  Depth K/16 + 16
+// instead of K.
+// --------------------------------------------------------------------------
+constexpr int kCombRows = 64;
+constexpr int kCombSegs = 16;
+
+__global__ __launch_bounds__(kCombRows * kCombSegs) void ssm_combine_scan_kernel(
+    const float* __restrict__ agg_p, const float* __restrict__ agg_h, const float* __restrict__ h0,
+    float* __restrict__ h_init, int64_t batch, int64_t dim, int64_t dstate, int64_t K) {
+  __shared__ float sP[kCombSegs][kCombRows], sH[kCombSegs][kCombRows];
+  const int64_t rows = batch * dstate * dim;
+  const int lane = threadIdx.x & (kCombRows - 1);
+  const int seg = threadIdx.x / kCombRows;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kCombRows + lane;
+  const bool valid = i < rows;
+  // segment seg covers chunks [k0, k1) (chunk K-1's total is never needed)
+  const int64_t per = (K + kCombSegs - 1) / kCombSegs;
+  const int64_t k0 = seg * per;
+  const int64_t k1 = (k0 + per < K) ? k0 + per : K;
+  float P = 1.0f, H = 0.0f;
+  if (valid) {
+    for (int64_t k = k0; k < k1 && k + 1 < K; ++k) {
+      const float p = agg_p[k * rows + i], hh = agg_h[k * rows + i];
+      H = __builtin_fmaf(p, H, hh);
+      P = p * P;
+    }
+  }
+  sP[seg][lane] = P;
+  sH[seg][lane] = H;
+  __syncthreads();
+  if (!valid) return;
+  // start state of the segment: h0, then the totals of segments 0 .. seg-1
+  const int64_t d = i % dim;
+  const int64_t n = (i / dim) % dstate;
+  const int64_t b = i / (dim * dstate);
+  float hv = h0 != nullptr ? h0[(b * dim + d) * dstate + n] : 0.0f;
+  for (int s = 0; s < seg; ++s) hv = __builtin_fmaf(sP[s][lane], hv, sH[s][lane]);
+  for (int64_t k = k0; k < k1; ++k) {
     h_init[k * rows + i] = hv;
     if (k + 1 < K) hv = __builtin_fmaf(agg_p[k * rows + i], hv, agg_h[k * rows + i]);
   }
@@ -796,6 +885,12 @@ hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t
 hipError_t launch_combine(const float* agg_p, const float* agg_h, const float* h0, float* h_init, int64_t batch,
                           int64_t dim, int64_t dstate, int64_t K, hipStream_t st) {
   const int64_t rows = batch * dstate * dim;
+  if (K >= kCombScanMinChunks) {
+    const unsigned blocks = static_cast<unsigned>((rows + kCombRows - 1) / kCombRows);
+    hipLaunchKernelGGL(ssm_combine_scan_kernel, dim3(blocks), dim3(kCombRows * kCombSegs), 0, st, agg_p, agg_h, h0,
+                       h_init, batch, dim, dstate, K);
+    return hipGetLastError();
+  }
   const unsigned blocks = static_cast<unsigned>((rows + 255) / 256);
   hipLaunchKernelGGL(ssm_combine_kernel, dim3(blocks), dim3(256), 0, st, agg_p, agg_h, h0, h_init, batch, dim, dstate,
                      K);

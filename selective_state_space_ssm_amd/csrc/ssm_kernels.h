@@ -54,6 +54,8 @@ hipError_t launch_rows_agg(const FwdArgs& a, bool bf16, int S, int64_t nchunks, 
 // remaining groups at S = 1 (one group per block).
 hipError_t launch_mixed_full(const FwdArgs& a, bool bf16, int64_t pairs, int64_t nchunks, hipStream_t st);
 // h0: [batch][dim][dstate] start state or null; rows = batch*dstate*dim.
+// With kCombScanMinChunks or more chunks the carry runs as a blocked scan.
+constexpr int64_t kCombScanMinChunks = 64;
 hipError_t launch_combine(const float* agg_p, const float* agg_h, const float* h0, float* h_init, int64_t batch,
                           int64_t dim, int64_t dstate, int64_t K, hipStream_t st);
 
