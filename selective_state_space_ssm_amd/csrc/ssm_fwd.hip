@@ -644,6 +644,13 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
 template <typename IO, int S, int MODE, bool GATED, bool VEC, bool CONV>
 __global__ __launch_bounds__(256 / S, 2) void ssm_rows_kernel(RowArgs<IO> args, CsSizes p) {
   extern __shared__ float smem[];
+  // One-wave workgroups (S = 4): reserving VGPR 175 keeps every such
+  // instantiation at 176 or more VGPRs, so a SIMD holds at most two of these
+  // waves.  A third resident wave (what 150 VGPRs would allow) made a
+  // 5120-workgroup bfloat16 launch (16 x 5120 x 16 x 8192) 25% slower, with
+  // 50% more instruction-wait cycles and the same VALU count; a cap through
+  // LDS size does not help, as it limits waves per CU, not per SIMD.
+  if constexpr (S == 4) asm volatile("" ::: "v175");
   const int tid = threadIdx.x;
   // the wave index as an SGPR keeps every per-wave quantity uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
