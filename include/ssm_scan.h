@@ -60,6 +60,14 @@ extern "C" {
                                that every SIMD carries the same number of
                                (channel, state) chains when the channel groups
                                number about three per CU */
+#define SSM_PLAN_LPAR    4  /* L-parallel single pass: workgroups of 4
+                               channels; each tile is cut into 16 time
+                               segments (one per lane of a row of 16) that
+                               fold thread-serially, are joined by a wave64
+                               DPP scan of their (prod a, h) pairs and refold
+                               from registers ([Scan page] §2.1, §3.2, §3.3).
+                               No chunk_states and no conv (SSM_EUNSUPPORTED
+                               if forced with either) */
 
 /*
  * ssm_scan_fwd -- selective-scan forward pass ([Scan page] §1.1-§1.2,
@@ -130,8 +138,9 @@ int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const
 /*
  * ssm_scan_fwd_plan -- ssm_scan_fwd with an explicit plan
  * ([Scan page] §2.2 and §3.3 describe both decompositions).
- *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY, SSM_PLAN_TWOPASS or
- *                     SSM_PLAN_MIXED (states_per_lane and chunk ignored).
+ *   plan            : SSM_PLAN_AUTO, SSM_PLAN_CARRY, SSM_PLAN_TWOPASS,
+ *                     SSM_PLAN_MIXED or SSM_PLAN_LPAR (states_per_lane and
+ *                     chunk ignored by the last two).
  *   states_per_lane : how many of the d_state states one lane carries for
  *                     its channel (1, 2 or 4; 0 = automatic).  A workgroup
  *                     covers 16 channels and 16 states with 4/states_per_lane

@@ -26,7 +26,7 @@ _lib = None
 
 SSM_OK, SSM_EINVAL, SSM_EUNSUPPORTED, SSM_EHIP, SSM_ENOMEM = 0, 1, 2, 3, 4
 SSM_F32, SSM_BF16 = 0, 1
-PLANS = {"auto": 0, "carry": 1, "twopass": 2, "mixed": 3}
+PLANS = {"auto": 0, "carry": 1, "twopass": 2, "mixed": 3, "lpar": 4}
 _PLAN_NAMES = {v: k for k, v in PLANS.items()}
 _STATUS = {SSM_EINVAL: "invalid argument", SSM_EUNSUPPORTED: "unsupported", SSM_EHIP: "HIP error",
            SSM_ENOMEM: "out of memory"}

@@ -13,6 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssmscan.so")
 SOURCES = ["ssm_fwd.hip", "ssm_bwd.hip", "ssm_step.hip", "ssm_proj.hip", "affine_scan.hip", "noalloc.hip",
+           "ssm_lpar.hip",
            "capi.cpp"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -85,7 +85,21 @@ int states_for(int64_t wgs) { return wgs >= 6 * kCUs ? 4 : 2; }
 // outweighs the extra cross-row sums; two in between.
 int bwd_states_for(int64_t groups) { return groups >= 8 * kCUs ? 4 : (groups >= 4 * kCUs ? 2 : 1); }
 
-void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out) {
+//  * L-parallel plan: workgroups of 4 channels whose tiles are cut into 16
+//    time segments, so a problem gets batch*d_inner wavefronts whatever L
+//    ([Scan page] §2.1, §3.2, §3.3).  Measured against the carry plan, it
+//    wins below 2.5 channel groups per CU (b=2 d=4096 L=2048: 103 vs 126 us;
+//    b=4 d=1536 L=2048: 82 vs 128 us; b=1 d=1536 L=512: 14 vs 28 us) and
+//    loses above (the 130m shape, 12288 channels: 175 vs 124 us for the mixed
+//    plan), where each lane's own chain is cheaper per step than fold,
+//    scan and refold.  Against the two-pass plan it wins once its wavefronts
+//    are at least 3/4 of the two-pass plan's (d=2048 L=65536: 786 vs 869 us;
+//    d=768 L=2048: 22 vs 97 us) and loses below (d=512 L=65536: 570 vs
+//    235 us).  Tiles are 256 steps, so L below 512 keeps the other plans.
+constexpr int64_t kLparMinL = 512;
+
+void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, int* S_out, int64_t* chunk_out,
+            bool lpar_ok = true) {
   (void)dstate;
   const int64_t groups = batch * ceil_div(dim, kGroup);
   int64_t chunk = L;
@@ -106,6 +120,15 @@ void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, in
       chunk = ceil_div(ceil_div(L, K), 64) * 64;
       pl = SSM_PLAN_TWOPASS;
       S = states_for(groups * ceil_div(L, chunk));
+    }
+  }
+  if (lpar_ok && groups < 5 * kCUs / 2 && L >= kLparMinL) {
+    const int64_t lpar_waves = batch * dim;
+    const int64_t tp_waves = pl == SSM_PLAN_TWOPASS ? groups * ceil_div(L, chunk) * (4 / S) : 0;
+    if (4 * lpar_waves >= 3 * tp_waves) {
+      pl = SSM_PLAN_LPAR;
+      S = ssm::kLparStates;
+      chunk = L;
     }
   }
   if (plan) *plan = pl;
@@ -147,8 +170,11 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (int rc = check_sizes(batch, dim, dstate, L)) return rc;
   if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_EUNSUPPORTED, "dtype %d is not supported", dtype);
   if (delta_softplus != 0 && delta_softplus != 1) return fail(SSM_EINVAL, "delta_softplus must be 0 or 1");
-  if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS && plan != SSM_PLAN_MIXED)
+  if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS && plan != SSM_PLAN_MIXED &&
+      plan != SSM_PLAN_LPAR)
     return fail(SSM_EINVAL, "unknown plan %d", plan);
+  if (plan == SSM_PLAN_LPAR && (chunk_states != nullptr || conv_w != nullptr))
+    return fail(SSM_EUNSUPPORTED, "the L-parallel plan takes neither chunk_states nor a conv");
   if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4)
     return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", S_req);
   if (chunk_req < 0 || chunk_req % 64 != 0) return fail(SSM_EINVAL, "chunk must be 0 or a positive multiple of 64");
@@ -184,7 +210,10 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
 
   int pl, S;
   int64_t chunk;
-  choose(batch, dim, dstate, L, &pl, &S, &chunk);
+  // a forced plan takes the states per lane and chunk of the choice among
+  // the other plans; the L-parallel plan has neither chunk states nor a conv
+  choose(batch, dim, dstate, L, &pl, &S, &chunk,
+         plan == SSM_PLAN_AUTO && chunk_states == nullptr && conv_w == nullptr);
   if (plan != SSM_PLAN_AUTO) pl = plan;
   if (S_req) S = S_req;
   if (S == 0) S = 2;  // states per lane of a carry or two-pass plan forced over a mixed choice
@@ -211,6 +240,12 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
     // fewer than three groups (a forced mixed plan) every block has one group
     const int64_t gd = ceil_div(dim, kGroup);
     hipError_t e = ssm::launch_mixed_full(a, bf16, gd / 3, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
+    return SSM_OK;
+  }
+  if (pl == SSM_PLAN_LPAR) {
+    a.chunk = L;
+    hipError_t e = ssm::launch_lpar(a, bf16, st);
     if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
     return SSM_OK;
   }

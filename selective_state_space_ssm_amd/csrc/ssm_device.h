@@ -269,6 +269,14 @@ __device__ __forceinline__ float delta2(float dl, float bias2, bool softplus) {
   return softplus ? softplus2(x2) : x2;
 }
 
+// delta2 with the softplus flag known at compile time (no branch per element).
+template <bool SP>
+__device__ __forceinline__ float delta2c(float dl, float bias2) {
+  const float x2 = __builtin_fmaf(dl, kLog2e, bias2);
+  if constexpr (SP) return softplus2(x2);
+  return x2;
+}
+
 // silu(z) = z / (1 + e^-z) ([Mamba-2 page] §4.1 SiLU gate).
 __device__ __forceinline__ float silu(float zz) {
   return zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * zz));

@@ -390,31 +390,38 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     const int r_t0 = R.t0;
     if constexpr (CONV) conv_front(R, r_t0);
     float dt[V], du[V];
-    if (r_t0 + kTT <= t_end) {
+    // softplus is one uniform branch around straight-line code per element
+    auto delta_full = [&](auto SP) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const float v2 = delta2(rd[e], bias2, softplus);
+        const float v2 = delta2c<decltype(SP)::value>(rd[e], bias2);
         dt[e] = v2;
         du[e] = (v2 * kLn2) * ru[e];
         nDu[e] = Dd * ru[e];
         nG[e] = kGate ? silu(rz[e]) : 1.0f;
       }
+    };
+    auto delta_part = [&](auto SP) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const bool ok = r_t0 + pt + e < t_end;
+        const float uu = ok ? ru[e] : 0.0f;
+        const float v2 = ok ? delta2c<decltype(SP)::value>(rd[e], bias2) : 0.0f;
+        dt[e] = v2;
+        du[e] = (v2 * kLn2) * uu;
+        nDu[e] = Dd * uu;
+        nG[e] = (kGate && ok) ? silu(rz[e]) : 1.0f;
+      }
+    };
+    if (r_t0 + kTT <= t_end) {
+      if (softplus) delta_full(std::true_type{}); else delta_full(std::false_type{});
       pin();
       F32::template st<V>(sDt + pc * kRow + pt, dt);
       F32::template st<V>(sDu + pc * kRow + pt, du);
 #pragma unroll
       for (int i = 0; i < BCQ; ++i) *reinterpret_cast<float4*>(sBC + bc_slot(tid + i * NT)) = rbc[i];
     } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const bool ok = r_t0 + pt + e < t_end;
-        const float uu = ok ? ru[e] : 0.0f;
-        const float v2 = ok ? delta2(rd[e], bias2, softplus) : 0.0f;
-        dt[e] = v2;
-        du[e] = (v2 * kLn2) * uu;
-        nDu[e] = Dd * uu;
-        nG[e] = (kGate && ok) ? silu(rz[e]) : 1.0f;
-      }
+      if (softplus) delta_part(std::true_type{}); else delta_part(std::false_type{});
       pin();
       F32::template st<V>(sDt + pc * kRow + pt, dt);
       F32::template st<V>(sDu + pc * kRow + pt, du);

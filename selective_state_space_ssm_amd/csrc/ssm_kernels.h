@@ -123,6 +123,14 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, int S, hipStream_t st);
 // Fill n floats with zero (a kernel, not a memset).
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 
+// L-parallel single-pass forward (ssm_lpar.hip): workgroups of 4 channels x
+// all states of one batch row; each tile is 16 segments of kLparSegSteps
+// steps, one per lane of a row of 16.  Takes u, delta, A, B, C, D, z, bias,
+// h0, y and last_state of `a` (no conv, no chunk states).
+constexpr int kLparStates = 4;     // states per lane (16/kLparStates wavefronts)
+constexpr int kLparSegSteps = 16;
+hipError_t launch_lpar(const FwdArgs& a, bool bf16, hipStream_t st);
+
 // Fixed per-device scratch of the entry point that allocates nothing
 // (noalloc.hip): its size in bytes, and its device address on the current
 // device (looked up once per device with hipGetSymbolAddress).

@@ -108,13 +108,19 @@ def test_plan_choice():
     assert p["plan"] == "mixed" and p["chunk"] == 2048  # 768 groups: three per CU
     p = ssm.plan_for(8, 4096, 16, 2048, "bf16")
     assert p["plan"] == "carry" and p["states_per_lane"] == 4
-    p = ssm.plan_for(4, 1536, 16, 2048)
-    assert p["plan"] == "carry" and p["states_per_lane"] == 2
     p = ssm.plan_for(16, 5120, 16, 8192, "bf16")
     assert p["plan"] == "carry"
+    # below 2.5 channel groups per CU: the L-parallel plan (4 states per lane)
+    p = ssm.plan_for(4, 1536, 16, 2048)
+    assert p["plan"] == "lpar" and p["states_per_lane"] == 4 and p["chunk"] == 2048
+    assert ssm.plan_for(1, 2048, 16, 65536)["plan"] == "lpar"
+    assert ssm.plan_for(1, 1536, 16, 512)["plan"] == "lpar"
+    # ... but not below 512 steps (256-step tiles)
+    assert ssm.plan_for(1, 1536, 16, 511)["plan"] == "carry"
     # few channels, very long sequence: two-pass over chunks that are multiples of 64
-    p = ssm.plan_for(1, 2048, 16, 65536)
+    p = ssm.plan_for(1, 512, 16, 65536)
     assert p["plan"] == "twopass" and p["chunk"] % 64 == 0 and 2 <= -(-65536 // p["chunk"]) <= 65535
+    assert ssm.plan_for(1, 16, 16, 1 << 20)["plan"] == "twopass"
     # short sequence never splits
     assert ssm.plan_for(1, 64, 16, 256)["plan"] == "carry"
     with pytest.raises(ssm.SSMError):

@@ -190,14 +190,16 @@ def test_identity_padding_varlen_small():
         assert rel_err(_host(last[bi, :8]), lref) <= 1e-4
 
 
-def test_softplus_off_zero_delta_pads():
-    """Softplus off with delta = 0 exactly at the padded steps (and no bias)."""
+@pytest.mark.parametrize("plan", ["carry", "lpar"])
+def test_softplus_off_zero_delta_pads(plan):
+    """Softplus off with delta = 0 exactly at the padded steps (and no bias):
+    under one plan, the final state equals the truncated run's bit for bit."""
     inp = small_inputs(3, 64, 16, 512, softplus=False, with_bias=False, seed=9)
     inp["delta"][:, :, 400:] = 0
-    check_all(inp)
-    _, last = run_gpu(inp)
+    check_all(inp, plan=plan)
+    _, last = run_gpu(inp, plan=plan)
     trunc = {k: (v[..., :400].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in inp.items()}
-    _, last_t = run_gpu(trunc)
+    _, last_t = run_gpu(trunc, plan=plan)
     assert torch.equal(last, last_t)
 
 
