@@ -152,14 +152,14 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "d95ae7d777032fe9", "plan": "mixed", "fetch_bytes": 333239025, "write_bytes": 101457033,
+    "130m": {"digest": "9f1cb20cc45ee176", "plan": "mixed", "fetch_bytes": 333314067, "write_bytes": 101452361,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "d95ae7d777032fe9", "plan": "carry", "fetch_bytes": 441692321, "write_bytes": 166576723,
+    "1.4b": {"digest": "9f1cb20cc45ee176", "plan": "carry", "fetch_bytes": 431370569, "write_bytes": 136511379,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "varlen": {"digest": "d95ae7d777032fe9", "plan": "carry", "fetch_bytes": 6473141997, "write_bytes": 1574714222,
+    "long": {"digest": "9f1cb20cc45ee176", "plan": "lpar", "fetch_bytes": 1204726862, "write_bytes": 537001984,
+             "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
+    "varlen": {"digest": "9f1cb20cc45ee176", "plan": "carry", "fetch_bytes": 6211635027, "write_bytes": 1350347925,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "d95ae7d777032fe9", "plan": "mixed", "fetch_bytes": 335528656, "write_bytes": 101450304,
-                   "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
 # The same for the bare affine scan (affine_scan.hip), keyed by workload.
@@ -199,7 +199,7 @@ MEASURED_BWD_TRAFFIC = {
 }
 
 
-def kernel_digest(sources=("ssm_fwd.hip", "ssm_device.h")) -> str:
+def kernel_digest(sources=("ssm_fwd.hip", "ssm_lpar.hip", "ssm_device.h")) -> str:
     """sha256 over the source of the given kernels (default: the forward scan)
     and the compiler flags they are built with: a stored traffic figure holds
     only for the build it was counted on."""
