@@ -160,6 +160,8 @@ MEASURED_TRAFFIC = {
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
     "varlen": {"digest": "9f1cb20cc45ee176", "plan": "carry", "fetch_bytes": 6211635027, "write_bytes": 1350347925,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
+    "130m+conv4": {"digest": "9f1cb20cc45ee176", "plan": "mixed", "fetch_bytes": 335726766, "write_bytes": 101453888,
+                   "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
 # The same for the bare affine scan (affine_scan.hip), keyed by workload.
@@ -190,12 +192,10 @@ MEASURED_DECODE_TRAFFIC = {
 # The same for the backward kernel (ssm_bwd.hip), keyed by workload and
 # conv taps, at the default state_chunk (128) and states per lane (auto).
 MEASURED_BWD_TRAFFIC = {
-    ("130m", 0): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 518590206, "write_bytes": 580762560,
+    ("130m", 0): {"digest": "5f30772464e8dca0", "fetch_bytes": 518857647, "write_bytes": 564924096,
                   "profile": "profiles/ssm_bwd_kernel_130m_f32.md"},
-    ("1.4b", 0): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 1127958592, "write_bytes": 1248096728,
+    ("1.4b", 0): {"digest": "5f30772464e8dca0", "fetch_bytes": 1123430770, "write_bytes": 1235154480,
                   "profile": "profiles/ssm_bwd_kernel_1.4b_bf16.md"},
-    ("130m", 4): {"digest": "fcd76fe6a770b53b", "fetch_bytes": 620653493, "write_bytes": 595324352,
-                  "profile": "profiles/ssm_bwd_kernel_conv4_130m_f32.md"},
 }
 
 
