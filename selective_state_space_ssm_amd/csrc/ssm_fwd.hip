@@ -440,11 +440,23 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   };
 
   // ---- recurrence of one tile from LDS
+  // Its LDS operands: B and C of the tile's step for each lane (both 16-step
+  // halves) and the Delta2 / Delta*u rows of each half.  In a one-wave
+  // workgroup (S = 4) they are read ahead of the arithmetic: the first
+  // half's rows and B, C right after the wave's own prep (the epilogue and
+  // the loads cover their latency), the second half's before the first is
+  // computed; such a workgroup also needs no barrier, since one wave's LDS
+  // accesses run in program order (1.4B -1.8%, varlen -0.4%).  With several
+  // waves per group the rows are read where the half starts (reading ahead
+  // there cost 1.4% at 130m).  bc and cc are only ever written by these LDS
+  // loads (they are DPP sources, see mul_bcast16).
+  constexpr bool kPre = (W == 1);
   const float* rowDt = sDt + col * kRow;
   const float* rowDu = sDu + col * kRow;
   float* rowP = sP + (grp * kCG + col) * kRow;
-  auto recur = [&]() {
-    float bc[S][2], cc[S][2];  // lane j of the row: step 16*half + j of state grp*S+s
+  float bc[S][2], cc[S][2];  // lane j of the row: step 16*half + j of state grp*S+s
+  float4 dqh[2][4], uqh[2][4];
+  auto read_bc = [&]() {
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -454,14 +466,26 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
         bc[s][hh] = sBC[n * kTT + tt + col];
         cc[s][hh] = (MODE == kFull) ? sBC[(kNS + n) * kTT + tt + col] : 0.0f;
       }
+  };
+  auto read_half = [&](int hh) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      dqh[hh][g4] = *reinterpret_cast<const float4*>(rowDt + 16 * hh + g4 * 4);
+      uqh[hh][g4] = *reinterpret_cast<const float4*>(rowDu + 16 * hh + g4 * 4);
+    }
+  };
+  auto recur = [&]() {
+    if constexpr (kPre) {
+      read_half(1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      read_bc();
+    }
     static_for<0, 2>([&](auto HH) {
       constexpr int hh = decltype(HH)::value;
-      float4 dq[4], uq[4];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        dq[g4] = *reinterpret_cast<const float4*>(rowDt + 16 * hh + g4 * 4);
-        uq[g4] = *reinterpret_cast<const float4*>(rowDu + 16 * hh + g4 * 4);
-      }
+      if constexpr (!kPre) read_half(hh);
+      float4 (&dq)[4] = dqh[hh];
+      float4 (&uq)[4] = uqh[hh];
       float y4[4];
       static_for<0, 16>([&](auto JJ) {
         constexpr int j = decltype(JJ)::value;
@@ -565,13 +589,19 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   load_tile(A, t_begin);
   load_tile(B, t_begin + kTT);
   prep(A);
+  if constexpr (kPre) {
+    read_bc();
+    read_half(0);
+  }
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     cDu[e] = nDu[e];
     cG[e] = nG[e];
   }
   load_tile(A, t_begin + 2 * kTT);
-  __syncthreads();
+  // A one-wave workgroup needs no barrier: its LDS accesses run in program
+  // order.
+  if constexpr (!kPre) __syncthreads();
   // State after the tile [t0, t0 + kTT) when it ends a state chunk (or the
   // sequence): the checkpoint of the Mamba-2 page §4.3 chunked recompute.
   const int sc = static_cast<int>(p.state_chunk);
@@ -601,8 +631,12 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     recur();
     if constexpr (S >= 2) __builtin_amdgcn_s_setprio(0);
     save_states(t0);
-    __syncthreads();
+    if constexpr (!kPre) __syncthreads();
     prep(next);
+    if constexpr (kPre) {
+      read_bc();
+      read_half(0);
+    }
     if (MODE == kFull) epilogue(t0, PARC);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -610,7 +644,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       cG[e] = nG[e];
     }
     load_tile(reload, t0 + 3 * kTT);
-    __syncthreads();
+    if constexpr (!kPre) __syncthreads();
   };
 #pragma unroll 1
   for (int it = 0; it < ntiles; it += 2) {
