@@ -58,10 +58,21 @@ struct F32 {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 struct BF16 {
   using T = uint16_t;
   static __device__ __forceinline__ uint32_t cvt(float f) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));  // RNE
+  }
+  // two values rounded to nearest even and packed (lo in bits 0-15): one
+  // v_cvt_pk_bf16_f32 on gfx950 instead of two conversions, a shift and an or
+  static __device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+    f32x2 v;
+    v.x = lo;
+    v.y = hi;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
   template <int V>
   static __device__ __forceinline__ void ld(const uint16_t* p, float* o) {
@@ -84,13 +95,13 @@ struct BF16 {
     if constexpr (V == 1) {
       *p = static_cast<uint16_t>(cvt(v[0]));
     } else if constexpr (V == 2) {
-      *reinterpret_cast<uint32_t*>(p) = cvt(v[0]) | (cvt(v[1]) << 16);
+      *reinterpret_cast<uint32_t*>(p) = cvt2(v[0], v[1]);
     } else if constexpr (V == 4) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(cvt(v[0]) | (cvt(v[1]) << 16), cvt(v[2]) | (cvt(v[3]) << 16));
+      *reinterpret_cast<uint2*>(p) = make_uint2(cvt2(v[0], v[1]), cvt2(v[2], v[3]));
     } else {
       *reinterpret_cast<uint4*>(p) =
-          make_uint4(cvt(v[0]) | (cvt(v[1]) << 16), cvt(v[2]) | (cvt(v[3]) << 16),
-                     cvt(v[4]) | (cvt(v[5]) << 16), cvt(v[6]) | (cvt(v[7]) << 16));
+          make_uint4(cvt2(v[0], v[1]), cvt2(v[2], v[3]),
+                     cvt2(v[4], v[5]), cvt2(v[6], v[7]));
     }
   }
 };
@@ -220,18 +231,18 @@ struct BufBF16 {
     if constexpr (V == 1) {
       __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(BF16::cvt(v[0])), r, off, 0, 0);
     } else if constexpr (V == 2) {
-      __builtin_amdgcn_raw_buffer_store_b32(BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(BF16::cvt2(v[0], v[1]), r, off, 0, 0);
     } else if constexpr (V == 4) {
       u32x2 w;
-      w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
-      w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+      w.x = BF16::cvt2(v[0], v[1]);
+      w.y = BF16::cvt2(v[2], v[3]);
       __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
     } else {
       u32x4 w;
-      w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
-      w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
-      w.z = BF16::cvt(v[4]) | (BF16::cvt(v[5]) << 16);
-      w.w = BF16::cvt(v[6]) | (BF16::cvt(v[7]) << 16);
+      w.x = BF16::cvt2(v[0], v[1]);
+      w.y = BF16::cvt2(v[2], v[3]);
+      w.z = BF16::cvt2(v[4], v[5]);
+      w.w = BF16::cvt2(v[6], v[7]);
       __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
     }
   }

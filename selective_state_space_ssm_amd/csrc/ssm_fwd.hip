@@ -561,7 +561,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       // the L2 whole rather than as two halves a tile apart.
       if (PAR == 0 && t0 + kTT <= t_end) {
 #pragma unroll
-        for (int e = 0; e < V / 2; ++e) yhold[e] = BF16::cvt(out[2 * e]) | (BF16::cvt(out[2 * e + 1]) << 16);
+        for (int e = 0; e < V / 2; ++e) yhold[e] = BF16::cvt2(out[2 * e], out[2 * e + 1]);
         return;
       }
       if (PAR == 1 && t0 <= t_end) store_words(poff + toff - kTT * ES, yhold);

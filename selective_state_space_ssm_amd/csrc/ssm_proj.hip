@@ -393,8 +393,8 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_gemm_kernel(GemmDev p) 
           __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
         } else {
           u32x2 w;
-          w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
-          w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+          w.x = BF16::cvt2(v[0], v[1]);
+          w.y = BF16::cvt2(v[2], v[3]);
           __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
         }
       } else {
@@ -677,8 +677,8 @@ __global__ void __launch_bounds__(kPThreads, 1) ssm_proj_dma_kernel(GemmDev p) {
       } else {
         const uint32_t off = (n < p.N && m < p.M) ? static_cast<uint32_t>(n * ldo + m) * ES : kOOB;
         u32x2 w;
-        w.x = BF16::cvt(v[0]) | (BF16::cvt(v[1]) << 16);
-        w.y = BF16::cvt(v[2]) | (BF16::cvt(v[3]) << 16);
+        w.x = BF16::cvt2(v[0], v[1]);
+        w.y = BF16::cvt2(v[2], v[3]);
         __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
       }
     }
