@@ -102,6 +102,8 @@ def parse():
     # a few hundred untimed steps (~0.1 s) let the GPU reach its steady clock
     p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--workload", default="130m")
+    p.add_argument("--shape", default="",
+                   help="B,D,N,L: the workload's recipe at other sizes (forward scan only; no traffic figure)")
     p.add_argument("--prewarm", type=float, default=PREWARM_S,
                    help="seconds of untimed launches after the warm-up steps (0: none, for counter runs)")
     p.add_argument("--plan", default="auto")
@@ -793,6 +795,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
+    if args.shape:
+        sb, sd, sn, sl = (int(x) for x in args.shape.split(","))
+        w = w.with_sizes(batch=sb, dim=sd, dstate=sn, L=sl)
     inp = workloads.make_inputs(w, device=dev, seed=0)
     y = torch.empty_like(inp["u"])
     last = torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32)
@@ -901,7 +906,8 @@ def main():
         plan = {"plan": args.plan, "states_per_lane": args.states_per_lane, "chunk": args.chunk, "explicit": True}
     tflops = w.state_steps() * FLOP_PER_STATE_STEP / (ms * 1e-3) / 1e12
     key = w.name + (f"+conv{args.conv}" if args.conv else "")
-    traffic = None if (use_states or args.conv_u_out or plan.get("explicit")) else measured_traffic(key, plan)
+    traffic = (None if (use_states or args.conv_u_out or plan.get("explicit") or args.shape)
+               else measured_traffic(key, plan))
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -920,7 +926,8 @@ def main():
                    "io_dtype": w.dtype, "gated": w.gated, "plan": plan,
                    **({"h0": True} if args.h0 else {}),
                    **({"conv_k": args.conv, "u_out": bool(args.conv_u_out)} if args.conv else {}),
-                   **({"state_chunk": args.state_chunk} if args.state_chunk else {})},
+                   **({"state_chunk": args.state_chunk} if args.state_chunk else {}),
+                   **({"sizes": "--shape " + args.shape} if args.shape else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "gsteps_ch_state_per_s": round(w.state_steps() / (ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
