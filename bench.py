@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "9f1cb20cc45ee176", "plan": "mixed", "fetch_bytes": 333314067, "write_bytes": 101452361,
+    "130m": {"digest": "78db5201d0aa6d9e", "plan": "mixed", "fetch_bytes": 333335907, "write_bytes": 101454433,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "9f1cb20cc45ee176", "plan": "carry", "fetch_bytes": 431370569, "write_bytes": 136511379,
+    "1.4b": {"digest": "78db5201d0aa6d9e", "plan": "carry", "fetch_bytes": 431252229, "write_bytes": 136562264,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "9f1cb20cc45ee176", "plan": "lpar", "fetch_bytes": 1204726862, "write_bytes": 537001984,
+    "long": {"digest": "78db5201d0aa6d9e", "plan": "lpar", "fetch_bytes": 1204720699, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "9f1cb20cc45ee176", "plan": "carry", "fetch_bytes": 6211635027, "write_bytes": 1350347925,
+    "varlen": {"digest": "78db5201d0aa6d9e", "plan": "carry", "fetch_bytes": 5348522982, "write_bytes": 1349193828,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "9f1cb20cc45ee176", "plan": "mixed", "fetch_bytes": 335726766, "write_bytes": 101453888,
+    "130m+conv4": {"digest": "78db5201d0aa6d9e", "plan": "mixed", "fetch_bytes": 335487307, "write_bytes": 101455943,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
