@@ -66,8 +66,8 @@ extern "C" {
                                fold thread-serially, are joined by a wave64
                                DPP scan of their (prod a, h) pairs and refold
                                from registers ([Scan page] §2.1, §3.2, §3.3).
-                               No chunk_states and no conv (SSM_EUNSUPPORTED
-                               if forced with either) */
+                               No conv in front (SSM_EUNSUPPORTED if forced
+                               with one) */
 
 /*
  * ssm_scan_fwd -- selective-scan forward pass ([Scan page] §1.1-§1.2,

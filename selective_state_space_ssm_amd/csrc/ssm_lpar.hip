@@ -42,6 +42,12 @@
 //         tile's carry-in (DPP row_newbcast:15).
 //   epi   (every thread): y = sum of the waves' partials + D*u, times
 //         silu(z), rounded to the storage type and stored.
+// Chunk states (the checkpoints of the chunked recompute, [Mamba-2 page]
+// §4.3): every state_chunk boundary is a multiple of 32 steps, so it falls on
+// the end of a segment, whose lane holds that state after its refold and
+// stores it.  Which segments of a tile end on a boundary is one 16-bit mask,
+// worked out by the scalar unit per tile.  The last entry, the state after
+// step L - 1, is the final carry, stored with last_state.
 // Two barriers per tile: prep | fold-scan-refold | epilogue + next prep.
 // Steps past L get Delta2 = 0, Delta*u = 0 and B = C = 0 (the identity
 // step, a = 1, b = 0); channels past d_inner and states past d_state read
@@ -129,17 +135,20 @@ struct LparArgs {
   typename IO::T* yg;
   float* last_state;    // nullable
   const float* h0;      // nullable
+  float* chunk_states;  // nullable: [b][nsc][d][n]
 };
 
 struct LparSizes {
   int64_t batch, dim, dstate, L;
+  int64_t nsc;          // chunk_states entries per batch row (0: none)
+  int sc;               // steps per entry, a multiple of 2*KS (0: none)
   int softplus;
 };
 
 // Template: storage IO, S states per lane (2 or 4: 16/S wavefronts), KS steps
 // per segment (tile = 16*KS steps), GATED (z present), VEC (L is a multiple
-// of 8: vector loads and stores).
-template <typename IO, int S, int KS, bool GATED, bool VEC>
+// of 8: vector loads and stores), CS (chunk states kept).
+template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS>
 __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args, LparSizes p) {
   using T = typename IO::T;
   using Buf = typename BufOf<IO>::type;
@@ -357,7 +366,22 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   const float* rowB = sB + wave * S * RS + j * SS;
   const float* rowC = sC + wave * S * RS + j * SS;
   float* rowY = sY + (wave * kLpCh + r) * RS + j * SS;
-  auto scan_tile = [&]() {
+  const int sc = p.sc;
+  // bmask: bit i set when segment i of the tile ends on a chunk boundary;
+  // kb: the boundaries before the tile (t0 / sc)
+  auto save_states = [&](const float* h, int t0, uint32_t bmask, int kb) {
+    if constexpr (!CS) return;
+    // the last entry (state after step L - 1) is the final carry, stored
+    // after the loop with last_state
+    const bool at = ((bmask >> j) & 1u) != 0 && t0 + (j + 1) * KS < Li && dvalid;
+    if (!at) return;
+    const int64_t k = kb + __builtin_popcount(bmask & ((2u << j) - 1u)) - 1;
+    float* dst = args.chunk_states + ((b * p.nsc + k) * dim + d) * N + static_cast<int64_t>(wave) * S;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (static_cast<int64_t>(wave) * S + s < N) dst[s] = h[s];
+  };
+  auto scan_tile = [&](int t0, uint32_t bmask, int kb) {
     float a[KS][S], bb[KS][S], H[S], P[S];
     float dsum = 0.0f;
 #pragma unroll
@@ -416,6 +440,7 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       }
       *reinterpret_cast<float4*>(rowY + 4 * q) = make_float4(yq[0], yq[1], yq[2], yq[3]);
     }
+    save_states(h, t0, bmask, kb);
 #pragma unroll
     for (int s = 0; s < S; ++s) carry[s] = row_last(h[s]);
   };
@@ -441,25 +466,37 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       for (int e = 0; e < V; ++e) Buf::template st<1>(rY, kDropOffset, &zero[e]);
     }
   }
+  int nxt = sc;  // steps from t0 to the next chunk boundary (1 .. sc)
+  int kb = 0;
   for (int t0 = 0; t0 < Li; t0 += TT) {
     prep(R, t0);
     load_tile(R, t0 + TT);
+    uint32_t bmask = 0;
+    const int kb_tile = kb;
+    if constexpr (CS) {
+      for (; nxt <= TT; nxt += sc, ++kb) bmask |= 1u << (nxt / KS - 1);
+      nxt -= TT;
+    }
     __syncthreads();
-    if (wave < WA) scan_tile();
+    if (wave < WA) scan_tile(t0, bmask, kb_tile);
     __syncthreads();
     epilogue(t0);
   }
 
-  if (args.last_state != nullptr && wave < WA && j == 0 && dvalid) {
+  if (wave < WA && j == 0 && dvalid) {
+    // the last chunk-state entry is the final state, bit for bit last_state
+    float* last_cs = CS ? args.chunk_states + ((b * p.nsc + p.nsc - 1) * dim + d) * N : nullptr;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int64_t n = static_cast<int64_t>(wave) * S + s;
-      if (n < N) args.last_state[(b * dim + d) * N + n] = carry[s];
+      if (n >= N) continue;
+      if (args.last_state != nullptr) args.last_state[(b * dim + d) * N + n] = carry[s];
+      if (last_cs != nullptr) last_cs[n] = carry[s];
     }
   }
 }
 
-template <typename IO, int S, int KS, bool GATED, bool VEC>
+template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS>
 static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   using T = typename IO::T;
   constexpr int RS = kLpSeg * (KS + 4);
@@ -468,11 +505,17 @@ static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   g.u = static_cast<const T*>(a.u); g.dlt = static_cast<const T*>(a.delta); g.Ag = a.A;
   g.Bg = static_cast<const T*>(a.B); g.Cg = static_cast<const T*>(a.C); g.Dg = a.D;
   g.zg = static_cast<const T*>(a.z); g.biasg = a.bias; g.yg = static_cast<T*>(a.y);
-  g.last_state = a.last_state; g.h0 = a.h0;
+  g.last_state = a.last_state; g.h0 = a.h0; g.chunk_states = a.chunk_states;
   LparSizes sz;
   sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.softplus = a.softplus;
+  const bool cs = a.chunk_states != nullptr && a.state_chunk > 0;
+  if (cs && a.state_chunk % (2 * KS) != 0) return hipErrorInvalidValue;
+  // a spacing of L or more has no boundary before step L; any multiple of 32
+  // past L then stands for it and fits an int
+  sz.sc = cs ? static_cast<int>(a.state_chunk <= a.L ? a.state_chunk : (a.L / 32 + 1) * 32) : 0;
+  sz.nsc = cs ? (a.L + a.state_chunk - 1) / a.state_chunk : 0;
   const dim3 grid(static_cast<unsigned>((a.dim + kLpCh - 1) / kLpCh), static_cast<unsigned>(a.batch));
-  auto kern = ssm_lpar_kernel<IO, S, KS, GATED, VEC>;
+  auto kern = ssm_lpar_kernel<IO, S, KS, GATED, VEC, CS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
@@ -480,13 +523,21 @@ static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, bool CS>
 static hipError_t dispatch_lpar(const FwdArgs& a, hipStream_t st) {
   constexpr int S = kLparStates, KS = kLparSegSteps;
   const bool vec = a.L % 8 == 0;
   if (a.z != nullptr)
-    return vec ? launch_lpar_v<IO, S, KS, true, true>(a, st) : launch_lpar_v<IO, S, KS, true, false>(a, st);
-  return vec ? launch_lpar_v<IO, S, KS, false, true>(a, st) : launch_lpar_v<IO, S, KS, false, false>(a, st);
+    return vec ? launch_lpar_v<IO, S, KS, true, true, CS>(a, st) : launch_lpar_v<IO, S, KS, true, false, CS>(a, st);
+  return vec ? launch_lpar_v<IO, S, KS, false, true, CS>(a, st) : launch_lpar_v<IO, S, KS, false, false, CS>(a, st);
+}
+
+template <typename IO>
+static hipError_t dispatch_lpar(const FwdArgs& a, hipStream_t st) {
+  // the chunk-state stores and their per-tile mask are compiled in only where
+  // they are asked for
+  return a.chunk_states != nullptr && a.state_chunk > 0 ? dispatch_lpar<IO, true>(a, st)
+                                                        : dispatch_lpar<IO, false>(a, st);
 }
 
 hipError_t launch_lpar(const FwdArgs& a, bool bf16, hipStream_t st) {

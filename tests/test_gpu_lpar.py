@@ -90,11 +90,58 @@ def test_lpar_start_state(L):
     assert rel_err(_host(last), last_ref) <= 1e-4
 
 
-def test_lpar_rejects_chunk_states():
-    inp = small_inputs(1, 8, 16, 64, seed=72)
-    with pytest.raises(ssm.SSMError, match="L-parallel"):
-        ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                                inp["delta_bias"], delta_softplus=True, state_chunk=32, plan="lpar")
+@pytest.mark.parametrize("L,sc", [(64, 32), (256, 32), (1000, 32), (1000, 96), (1024, 128), (1500, 128),
+                                  (2048, 224), (3000, 512), (700, 4096), (2048, 2048)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_lpar_chunk_states(L, sc, dtype):
+    """The states at every state_chunk boundary (the checkpoints the backward
+    recomputes from) through the L-parallel plan, from a start state: spacings
+    below, at and above the 256-step tile, not dividing it (96, 224), L a
+    multiple of the spacing or not, and a spacing longer than L (one entry,
+    the final state).  Every entry against the oracle's states at the same
+    steps."""
+    b, d, n = 2, 21, 13
+    inp = small_inputs(b, d, n, L, dtype=dtype, seed=80 + L + sc)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(81)
+    h0 = torch.randn((b, d, n), generator=g, device=DEV, dtype=torch.float32)
+    y, last, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                          inp["delta_bias"], delta_softplus=True, h0=h0, state_chunk=sc, plan="lpar")
+    torch.cuda.synchronize(DEV)
+    y_ref, last_ref, bounds = ref.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                                     inp["z"], inp["delta_bias"], True, h0=h0, chunk=sc)
+    K = -(-L // sc)
+    assert cs.shape == (b, K, d, n)
+    cs_ref = bounds[..., 1:].transpose(0, 3, 1, 2)  # [b, K, d, n]
+    assert rel_err(_host(cs), cs_ref) <= 1e-4
+    assert rel_err(_host(y), y_ref) <= TOL[dtype]
+    assert rel_err(_host(last), last_ref) <= 1e-4
+    np.testing.assert_array_equal(_host(cs)[:, -1], _host(last))
+
+
+def test_lpar_chunk_states_feed_the_backward():
+    """The backward from the L-parallel plan's chunk states gives the same
+    gradients as from the carry plan's (both are the state after the same
+    steps, to float32 rounding)."""
+    inp = small_inputs(1, 40, 16, 1024, seed=82)
+    sc = 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(83)
+    dy = torch.randn(inp["u"].shape, generator=g, device=DEV, dtype=inp["u"].dtype)
+    grads = []
+    for plan in ("lpar", "carry"):
+        _, _, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                           inp["delta_bias"], delta_softplus=True, state_chunk=sc, plan=plan)
+        gr = ssm.ssm_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, dy, D=inp["D"],
+                              z=inp["z"], delta_bias=inp["delta_bias"], delta_softplus=True)
+        grads.append(gr)
+    torch.cuda.synchronize(DEV)
+    for name in grads[0]:
+        if grads[0][name] is None:
+            continue
+        a, c = _host(grads[0][name]), _host(grads[1][name])
+        assert rel_err(a, c) <= 1e-4, name
 
 
 def test_lpar_extreme_values():
@@ -173,7 +220,8 @@ def _sweep_cases(seed, count):
                         dtype=(torch.float32, torch.bfloat16)[int(rng.integers(2))],
                         gated=bool(rng.integers(2)), with_D=bool(rng.integers(2)),
                         with_bias=bool(rng.integers(2)), softplus=bool(rng.integers(2)),
-                        h0=bool(rng.integers(2)), seed=int(rng.integers(1 << 20))))
+                        h0=bool(rng.integers(2)), seed=int(rng.integers(1 << 20)),
+                        sc=int(rng.choice([0, 32, 96, 128, 512]))))
     return out
 
 
@@ -181,11 +229,13 @@ SWEEP = _sweep_cases(7909, 24)
 
 
 @pytest.mark.parametrize("c", SWEEP, ids=lambda c: f"b{c['b']}d{c['d']}n{c['n']}L{c['L']}"
-                         f"{'-bf16' if c['dtype'] == torch.bfloat16 else ''}{'-h0' if c['h0'] else ''}")
+                         f"{'-bf16' if c['dtype'] == torch.bfloat16 else ''}{'-h0' if c['h0'] else ''}"
+                         f"{'-sc' + str(c['sc']) if c['sc'] else ''}")
 def test_lpar_seeded_sweep(c):
     """Seeded random sizes (ragged channels, states, segments and tiles, L
-    from 1), storage types, optional inputs and start states through the
-    L-parallel plan, every element against the float64 oracle."""
+    from 1), storage types, optional inputs, start states and chunk-state
+    spacings through the L-parallel plan, every element against the float64
+    oracle."""
     inp = small_inputs(c["b"], c["d"], c["n"], c["L"], dtype=c["dtype"], gated=c["gated"], with_D=c["with_D"],
                        with_bias=c["with_bias"], softplus=c["softplus"], seed=c["seed"])
     h0 = None
@@ -193,11 +243,16 @@ def test_lpar_seeded_sweep(c):
         g = torch.Generator(device=DEV)
         g.manual_seed(c["seed"] + 7)
         h0 = torch.randn((c["b"], c["d"], c["n"]), generator=g, device=DEV, dtype=torch.float32)
-    y, last, _ = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                                         inp["delta_bias"], delta_softplus=inp["delta_softplus"], h0=h0, plan="lpar")
+    sc = c["sc"]
+    y, last, cs = ssm.ssm_scan_fwd_states(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                          inp["delta_bias"], delta_softplus=inp["delta_softplus"], h0=h0,
+                                          state_chunk=sc, plan="lpar")
     torch.cuda.synchronize(DEV)
-    y_ref, last_ref = ref.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
-                                             inp["z"], inp["delta_bias"], inp["delta_softplus"], h0=h0)
+    res = ref.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                 inp["delta_bias"], inp["delta_softplus"], h0=h0, chunk=sc or None)
+    y_ref, last_ref = res[0], res[1]
     tol = TOL[c["dtype"]]
     assert rel_err(_host(y), y_ref) <= tol
     assert rel_err(_host(last), last_ref) <= 1e-4
+    if sc:
+        assert rel_err(_host(cs), res[2][..., 1:].transpose(0, 3, 1, 2)) <= 1e-4
