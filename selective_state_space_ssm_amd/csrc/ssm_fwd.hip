@@ -584,10 +584,24 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   // nothing stores): a conditional load would make the compiler copy its
   // result at the join and wait for it there.  An odd tile count runs one
   // extra all-identity tile.
+  // bfloat16 in a one-wave group: a tile's row slice is 64 bytes, half of a
+  // 128-byte line, and the two halves of a line, loaded a tile apart, met in
+  // the L2 only when the line survived that long: with row strides of a
+  // power of two (L = 8192: 16 KB) the lines of all rows fall into the same
+  // few L2 sets and the varlen shape fetched 1.33x its input bytes (1.04x at
+  // L = 8256).  Such groups load a line's two halves together instead: four
+  // register sets (A, B, then A2, B2: tiles 4i .. 4i+3), refilled two at a
+  // time, the loop unrolled by four; the last loads run up to seven tiles
+  // ahead and 0 to 3 all-identity tiles close the chunk.
+  constexpr bool kPairLoads = std::is_same<IO, BF16>::value && VEC && S == 4 && !CONV;
   const int ntiles = (t_end - t_begin + kTT - 1) / kTT;
-  TileRegs A, B;
+  TileRegs A, B, A2, B2;
   load_tile(A, t_begin);
   load_tile(B, t_begin + kTT);
+  if constexpr (kPairLoads) {
+    load_tile(A2, t_begin + 2 * kTT);
+    load_tile(B2, t_begin + 3 * kTT);
+  }
   prep(A);
   if constexpr (kPre) {
     read_bc();
@@ -598,7 +612,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     cDu[e] = nDu[e];
     cG[e] = nG[e];
   }
-  load_tile(A, t_begin + 2 * kTT);
+  if constexpr (!kPairLoads) load_tile(A, t_begin + 2 * kTT);
   // A one-wave workgroup needs no barrier: its LDS accesses run in program
   // order.
   if constexpr (!kPre) __syncthreads();
@@ -621,7 +635,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       if (n < N) chunk_states[((b * nsc + kc) * dim + d) * N + n] = h[s];
     }
   };
-  auto half_step = [&](int t0, TileRegs& next, TileRegs& reload, auto PARC) {
+  auto half_step = [&](int t0, TileRegs& next, auto PARC, auto&& loads) {
     // With two or more states per lane the recurrence is a long VALU stream
     // while the other waves of the SIMD sit in the latency-bound prep and
     // epilogue: raising this wave's issue priority for the recurrence keeps
@@ -643,14 +657,33 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       cDu[e] = nDu[e];
       cG[e] = nG[e];
     }
-    load_tile(reload, t0 + 3 * kTT);
+    loads();
     if constexpr (!kPre) __syncthreads();
   };
+  constexpr std::integral_constant<int, 0> kEven{};
+  constexpr std::integral_constant<int, 1> kOdd{};
+  if constexpr (kPairLoads) {
 #pragma unroll 1
-  for (int it = 0; it < ntiles; it += 2) {
-    const int t0 = t_begin + it * kTT;
-    half_step(t0, B, B, std::integral_constant<int, 0>{});
-    half_step(t0 + kTT, A, A, std::integral_constant<int, 1>{});
+    for (int it = 0; it < ntiles; it += 4) {
+      const int t0 = t_begin + it * kTT;
+      half_step(t0, B, kEven, [&] {
+        load_tile(A, t0 + 4 * kTT);
+        load_tile(B, t0 + 5 * kTT);
+      });
+      half_step(t0 + kTT, A2, kOdd, [] {});
+      half_step(t0 + 2 * kTT, B2, kEven, [&] {
+        load_tile(A2, t0 + 6 * kTT);
+        load_tile(B2, t0 + 7 * kTT);
+      });
+      half_step(t0 + 3 * kTT, A, kOdd, [] {});
+    }
+  } else {
+#pragma unroll 1
+    for (int it = 0; it < ntiles; it += 2) {
+      const int t0 = t_begin + it * kTT;
+      half_step(t0, B, kEven, [&] { load_tile(B, t0 + 3 * kTT); });
+      half_step(t0 + kTT, A, kOdd, [&] { load_tile(A, t0 + 4 * kTT); });
+    }
   }
 
   // ---- chunk end: final state or chunk aggregate
