@@ -19,8 +19,11 @@
 //   prep  (every thread): Delta2 = softplus(delta + bias) in log2 units and
 //         Delta*u of the tile's 4 channels, and B and C of its 16 states,
 //         into LDS (float32); D*u and silu(z) stay in registers for the
-//         epilogue.  The global loads of the next tile are issued right
-//         after, so they have the whole scan to arrive.
+//         epilogue.  The global loads are issued right after: B and C of
+//         the next tile (read by every workgroup of the batch row, mostly
+//         L2 hits) and u, delta, z of the tile after it (two register sets,
+//         the loop unrolled by two), so that the HBM reads have two tiles
+//         to arrive.
 //   fold  (every lane, thread-serial over its KS steps and four states):
 //         a = exp2(Delta2 * A), b = (Delta*u) * B, kept in registers, and
 //         the segment's pair (P, H): P = prod a = exp2(A * sum Delta2), H =
@@ -241,11 +244,13 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   constexpr int RW = VEC ? Buf::template kWords<V> : V;
   constexpr int KC = KS < 8 ? KS : 8;  // B/C elements per load (at most 8 bfloat16 in one b128)
   constexpr int BW = VEC ? (KS / KC) * Buf::template kWords<KC> : KS;
-  struct TileRegs {
+  struct UDRegs {
     uint32_t wu[RW], wd[RW], wz[RW];
+  };
+  struct BCRegs {
     uint32_t wbc[NBC][BW];
   };
-  auto load_tile = [&](TileRegs& R, int t0) {
+  auto load_ud = [&](UDRegs& R, int t0) {
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
     if (!GATED) {
 #pragma unroll
@@ -255,6 +260,18 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       Buf::template ldw<V>(rU, poff + toff, R.wu);
       Buf::template ldw<V>(rD, poff + toff, R.wd);
       if (GATED) Buf::template ldw<V>(rZ, poff + toff, R.wz);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        Buf::template ldw<1>(rU, poff + toff + e * ES, &R.wu[e]);
+        Buf::template ldw<1>(rD, poff + toff + e * ES, &R.wd[e]);
+        if (GATED) Buf::template ldw<1>(rZ, poff + toff + e * ES, &R.wz[e]);
+      }
+    }
+  };
+  auto load_bc = [&](BCRegs& R, int t0) {
+    const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+    if constexpr (VEC) {
 #pragma unroll
       for (int q = 0; q < NBC; ++q)
 #pragma unroll
@@ -263,12 +280,6 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
                                 R.wbc[q] + (i / KC) * Buf::template kWords<KC>);
     } else {
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        Buf::template ldw<1>(rU, poff + toff + e * ES, &R.wu[e]);
-        Buf::template ldw<1>(rD, poff + toff + e * ES, &R.wd[e]);
-        if (GATED) Buf::template ldw<1>(rZ, poff + toff + e * ES, &R.wz[e]);
-      }
-#pragma unroll
       for (int q = 0; q < NBC; ++q)
 #pragma unroll
         for (int e = 0; e < KS; ++e) Buf::template ldw<1>(bcis_c[q] ? rC : rB, bcoff[q] + toff + e * ES, &R.wbc[q][e]);
@@ -276,21 +287,21 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   };
 
   float nDu[V], nG[V];
-  auto prep = [&](TileRegs& R, int t0) {
+  auto prep = [&](UDRegs& R, BCRegs& RB, int t0) {
     // the loaded words are pinned so that no conversion moves ahead of here
 #pragma unroll
     for (int e = 0; e < RW; ++e) asm volatile("" : "+v"(R.wu[e]), "+v"(R.wd[e]), "+v"(R.wz[e]));
 #pragma unroll
     for (int q = 0; q < NBC; ++q)
 #pragma unroll
-      for (int e = 0; e < BW; ++e) asm volatile("" : "+v"(R.wbc[q][e]));
+      for (int e = 0; e < BW; ++e) asm volatile("" : "+v"(RB.wbc[q][e]));
     float ru[V], rd[V], rz[V], rbc[NBC][KS];
     if constexpr (VEC) {
       Buf::template unpack<V>(R.wu, ru);
       Buf::template unpack<V>(R.wd, rd);
       Buf::template unpack<V>(R.wz, rz);
 #pragma unroll
-      for (int q = 0; q < NBC; ++q) Buf::template unpack<KS>(R.wbc[q], rbc[q]);
+      for (int q = 0; q < NBC; ++q) Buf::template unpack<KS>(RB.wbc[q], rbc[q]);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
 #pragma unroll
       for (int q = 0; q < NBC; ++q)
 #pragma unroll
-        for (int e = 0; e < KS; ++e) Buf::template unpack<1>(&R.wbc[q][e], &rbc[q][e]);
+        for (int e = 0; e < KS; ++e) Buf::template unpack<1>(&RB.wbc[q][e], &rbc[q][e]);
     }
     // whole tiles take no per-element masks; softplus is one uniform branch
     float dt[V], du[V];
@@ -445,16 +456,23 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
     for (int s = 0; s < S; ++s) carry[s] = row_last(h[s]);
   };
 
-  // The next tile's loads are issued on every tile, the last one included
-  // (reads past L return words of the next row or zero past the resource,
-  // and prep never uses them), so that no branch makes the wait for them
-  // conservative.
-  // After the first loads, as many stores as one epilogue issues (dropped,
-  // past the resource): the wait at the top of the loop then sees the same
-  // count of memory operations after the loads on entry as on every later
-  // tile, so it waits for the loads only.
-  TileRegs R;
-  load_tile(R, 0);
+  // The loads are issued on every tile, the last ones included (reads past
+  // L return words of the next row or zero past the resource, and prep never
+  // uses them), so that no branch makes the wait for them conservative.
+  // The first loads go out in the order of every later tile (u/delta/z of
+  // tile 0, B/C of tile 0, then u/delta/z of tile 1: the scheduling barriers
+  // keep the compiler from interleaving them), followed by as many stores
+  // as one epilogue issues (dropped, past the resource): the wait at the top
+  // of the loop then sees the same count of memory operations after each
+  // set of loads on entry as on every later pair of tiles, so it waits for
+  // the loads only.
+  UDRegs U0, U1;
+  BCRegs RB;
+  load_ud(U0, 0);
+  load_bc(RB, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_ud(U1, TT);
+  __builtin_amdgcn_sched_barrier(0);
   {
     float zero[V];
 #pragma unroll
@@ -468,9 +486,14 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   }
   int nxt = sc;  // steps from t0 to the next chunk boundary (1 .. sc)
   int kb = 0;
-  for (int t0 = 0; t0 < Li; t0 += TT) {
-    prep(R, t0);
-    load_tile(R, t0 + TT);
+  // A tile that starts at or past L (the second of the last pair when the
+  // tile count is odd) is all identity steps: its prep, loads and (dropped)
+  // stores still run, so that every tile issues the same memory operations,
+  // but its scan is skipped (the carry would come out unchanged).
+  auto tile = [&](UDRegs& U, int t0) {
+    prep(U, RB, t0);
+    load_bc(RB, t0 + TT);
+    load_ud(U, t0 + 2 * TT);
     uint32_t bmask = 0;
     const int kb_tile = kb;
     if constexpr (CS) {
@@ -478,9 +501,13 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       nxt -= TT;
     }
     __syncthreads();
-    if (wave < WA) scan_tile(t0, bmask, kb_tile);
+    if (wave < WA && t0 < Li) scan_tile(t0, bmask, kb_tile);
     __syncthreads();
     epilogue(t0);
+  };
+  for (int t0 = 0; t0 < Li; t0 += 2 * TT) {
+    tile(U0, t0);
+    tile(U1, t0 + TT);
   }
 
   if (wave < WA && j == 0 && dvalid) {
