@@ -446,13 +446,25 @@ int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* 
   // (spills) and LDS (occupancy): two measured faster at the 1.4B shape
   if (states_per_lane == 0 && conv_w != nullptr && S == 4) S = 2;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = ssm::launch_zero(dA, int64_t(ndn), st);
-  if (e == hipSuccess) e = ssm::launch_zero(dB, int64_t(nbnl), st);
-  if (e == hipSuccess) e = ssm::launch_zero(dC, int64_t(nbnl), st);
-  if (e == hipSuccess && dD) e = ssm::launch_zero(dD, d_inner, st);
-  if (e == hipSuccess && ddelta_bias) e = ssm::launch_zero(ddelta_bias, d_inner, st);
-  if (e == hipSuccess && conv_w) e = ssm::launch_zero(dconv_w, d_inner * conv_k, st);
-  if (e == hipSuccess && conv_w && dconv_b) e = ssm::launch_zero(dconv_b, d_inner, st);
+  // every output that the kernel sums into with atomics, cleared by one launch
+  ssm::ZeroList zl{};
+  auto clear = [&](float* q, int64_t n) {
+    if (q != nullptr && n > 0) {
+      zl.p[zl.count] = q;
+      zl.n[zl.count] = n;
+      ++zl.count;
+    }
+  };
+  clear(dA, int64_t(ndn));
+  clear(dB, int64_t(nbnl));
+  clear(dC, int64_t(nbnl));
+  clear(dD, d_inner);
+  clear(ddelta_bias, d_inner);
+  if (conv_w) {
+    clear(dconv_w, d_inner * conv_k);
+    clear(dconv_b, d_inner);
+  }
+  hipError_t e = ssm::launch_zero(zl, st);
   if (e != hipSuccess) return hip_fail(e, "gradient clear launch");
   ssm::BwdArgs a{};
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;

@@ -836,7 +836,11 @@ __global__ __launch_bounds__(256 / S, S == 1 ? 3 : 2) void ssm_bwd_kernel(BwdDev
   }
 }
 
-__global__ __launch_bounds__(256) void ssm_zero_kernel(float* __restrict__ p, int64_t n) {
+// Clears up to kZeroBufs float buffers in one launch: grid row y clears
+// buffer y with a grid-stride loop over x.
+__global__ __launch_bounds__(256) void ssm_zero_kernel(ZeroList z) {
+  float* __restrict__ p = z.p[blockIdx.y];
+  const int64_t n = z.n[blockIdx.y];
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
@@ -906,11 +910,16 @@ hipError_t launch_bwd(const BwdArgs& h, bool bf16, int S, hipStream_t st) {
   return S == 2 ? launch_bwd_s<F32, 2>(h, st) : launch_bwd_s<F32, 1>(h, st);
 }
 
-hipError_t launch_zero(float* p, int64_t n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
+hipError_t launch_zero(const ZeroList& z, hipStream_t st) {
+  if (z.count <= 0) return hipSuccess;
+  if (z.count > kZeroBufs) return hipErrorInvalidValue;
+  int64_t most = 0;
+  for (int i = 0; i < z.count; ++i) most = z.n[i] > most ? z.n[i] : most;
+  int64_t blocks = (most + 255) / 256;
+  if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(ssm_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, n);
+  hipLaunchKernelGGL(ssm_zero_kernel, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(z.count)), dim3(256),
+                     0, st, z);
   return hipGetLastError();
 }
 

@@ -121,7 +121,15 @@ constexpr int kBwdMaxChunk = 512;  // largest state_chunk (LDS holds one state p
 size_t bwd_smem_bytes(int S, int64_t state_chunk, bool conv);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int S, hipStream_t st);
 // Fill n floats with zero (a kernel, not a memset).
-hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
+// Float buffers to clear with one launch (n[i] elements at p[i]; count of
+// them used, at most kZeroBufs).
+constexpr int kZeroBufs = 8;
+struct ZeroList {
+  float* p[kZeroBufs];
+  int64_t n[kZeroBufs];
+  int count;
+};
+hipError_t launch_zero(const ZeroList& z, hipStream_t st);
 
 // L-parallel single-pass forward (ssm_lpar.hip): workgroups of 4 channels x
 // all states of one batch row; each tile is 16 segments of kLparSegSteps
