@@ -65,9 +65,7 @@ extern "C" {
                                segments (one per lane of a row of 16) that
                                fold thread-serially, are joined by a wave64
                                DPP scan of their (prod a, h) pairs and refold
-                               from registers ([Scan page] §2.1, §3.2, §3.3).
-                               No conv in front (SSM_EUNSUPPORTED if forced
-                               with one) */
+                               from registers ([Scan page] §2.1, §3.2, §3.3) */
 
 /*
  * ssm_scan_fwd -- selective-scan forward pass ([Scan page] §1.1-§1.2,

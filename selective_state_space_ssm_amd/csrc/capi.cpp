@@ -173,8 +173,6 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   if (plan != SSM_PLAN_AUTO && plan != SSM_PLAN_CARRY && plan != SSM_PLAN_TWOPASS && plan != SSM_PLAN_MIXED &&
       plan != SSM_PLAN_LPAR)
     return fail(SSM_EINVAL, "unknown plan %d", plan);
-  if (plan == SSM_PLAN_LPAR && conv_w != nullptr)
-    return fail(SSM_EUNSUPPORTED, "the L-parallel plan takes no conv");
   if (S_req != 0 && S_req != 1 && S_req != 2 && S_req != 4)
     return fail(SSM_EINVAL, "states_per_lane must be 0, 1, 2 or 4 (got %d)", S_req);
   if (chunk_req < 0 || chunk_req % 64 != 0) return fail(SSM_EINVAL, "chunk must be 0 or a positive multiple of 64");
@@ -211,8 +209,8 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   int pl, S;
   int64_t chunk;
   // a forced plan takes the states per lane and chunk of the choice among
-  // the other plans; the L-parallel plan has no conv in front
-  choose(batch, dim, dstate, L, &pl, &S, &chunk, plan == SSM_PLAN_AUTO && conv_w == nullptr);
+  // the other plans
+  choose(batch, dim, dstate, L, &pl, &S, &chunk, plan == SSM_PLAN_AUTO);
   if (plan != SSM_PLAN_AUTO) pl = plan;
   if (S_req) S = S_req;
   if (S == 0) S = 2;  // states per lane of a carry or two-pass plan forced over a mixed choice

@@ -16,7 +16,9 @@
 // (r, j) of a wave (row r = lane / 16, j = lane % 16) holds channel c0 + r
 // over time segment j of the current tile: the tile of 16*KS steps is cut
 // into 16 segments of KS steps, one per lane of the row.  Per tile:
-//   prep  (every thread): Delta2 = softplus(delta + bias) in log2 units and
+//   prep  (every thread): with the conv in front, u = silu(causal conv1d
+//         of x) from x and the 3 steps before each thread's slot (stored
+//         when asked for); Delta2 = softplus(delta + bias) in log2 units and
 //         Delta*u of the tile's 4 channels, and B and C of its 16 states,
 //         into LDS (float32); D*u and silu(z) stay in registers for the
 //         epilogue.  The global loads are issued right after: B and C of
@@ -139,6 +141,9 @@ struct LparArgs {
   float* last_state;    // nullable
   const float* h0;      // nullable
   float* chunk_states;  // nullable: [b][nsc][d][n]
+  const float* convw;   // CONV: [d][K] causal conv1d weights (u then points at x)
+  const float* convb;   // CONV: [d] conv bias, nullable
+  typename IO::T* uo;   // CONV: [b][d][L] silu(conv1d(x)) output, nullable
 };
 
 struct LparSizes {
@@ -146,12 +151,14 @@ struct LparSizes {
   int64_t nsc;          // chunk_states entries per batch row (0: none)
   int sc;               // steps per entry, a multiple of 2*KS (0: none)
   int softplus;
+  int convk;            // CONV: conv1d taps, 1..4
 };
 
 // Template: storage IO, S states per lane (2 or 4: 16/S wavefronts), KS steps
 // per segment (tile = 16*KS steps), GATED (z present), VEC (L is a multiple
-// of 8: vector loads and stores), CS (chunk states kept).
-template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS>
+// of 8: vector loads and stores), CS (chunk states kept), CONV (u =
+// silu(causal conv1d of x) computed in prep from x, [Mamba-2 page] §4.1).
+template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS, bool CONV>
 __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args, LparSizes p) {
   using T = typename IO::T;
   using Buf = typename BufOf<IO>::type;
@@ -211,6 +218,17 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   const bool pvalid = pd < dim;
   const float bias2 = (pvalid && args.biasg != nullptr) ? args.biasg[pd] * kLog2e : 0.0f;
   const float Dd = (pvalid && args.Dg != nullptr) ? args.Dg[pd] : 0.0f;
+  // CONV: the K taps right-aligned in w4 (w4[3] multiplies x_t, w4[3-j]
+  // multiplies x_{t-j}); x before step 0 is zero
+  float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cbias = 0.0f;
+  if constexpr (CONV) {
+    const int K = p.convk;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (pvalid && jj >= 4 - K) w4[jj] = args.convw[pd * K + (jj - (4 - K))];
+    cbias = (pvalid && args.convb != nullptr) ? args.convb[pd] : 0.0f;
+  }
 
   // Buffer resources over the workgroup's rows of u, delta, z, y and over
   // batch row b of B and C: channels past d_inner and states past d_state
@@ -222,6 +240,10 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   const Rsrc rD = make_rsrc(dlt + row0, in_bytes);
   const Rsrc rZ = make_rsrc(GATED ? zg + row0 : u + row0, in_bytes);
   const Rsrc rY = make_rsrc(yg + row0, in_bytes);
+  // CONV: silu(conv1d(x)) out, when asked for (else an empty resource: the
+  // stores still issue, and drop)
+  const bool uo_on = CONV && args.uo != nullptr;
+  const Rsrc rUO = make_rsrc(uo_on ? args.uo + row0 : yg + row0, uo_on ? in_bytes : 0u);
   const uint32_t bc_bytes = static_cast<uint32_t>(N * L * ES);
   const Rsrc rB = make_rsrc(args.Bg + b * N * L, bc_bytes);
   const Rsrc rC = make_rsrc(args.Cg + b * N * L, bc_bytes);
@@ -244,8 +266,10 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   constexpr int RW = VEC ? Buf::template kWords<V> : V;
   constexpr int KC = KS < 8 ? KS : 8;  // B/C elements per load (at most 8 bfloat16 in one b128)
   constexpr int BW = VEC ? (KS / KC) * Buf::template kWords<KC> : KS;
+  constexpr int HW = CONV ? 3 : 1;  // CONV: x at the 3 steps before the slot
   struct UDRegs {
     uint32_t wu[RW], wd[RW], wz[RW];
+    uint32_t wh[HW];
   };
   struct BCRegs {
     uint32_t wbc[NBC][BW];
@@ -255,6 +279,14 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
     if (!GATED) {
 #pragma unroll
       for (int e = 0; e < RW; ++e) R.wz[e] = 0u;
+    }
+    if constexpr (CONV) {
+      // before step 0 of the first channel the offset wraps past the
+      // resource and reads zero; prep zeroes the other rows' tails
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) Buf::template ldw<1>(rU, poff + toff - (3 - jj) * ES, &R.wh[jj]);
+    } else {
+      R.wh[0] = 0u;
     }
     if constexpr (VEC) {
       Buf::template ldw<V>(rU, poff + toff, R.wu);
@@ -292,6 +324,8 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
 #pragma unroll
     for (int e = 0; e < RW; ++e) asm volatile("" : "+v"(R.wu[e]), "+v"(R.wd[e]), "+v"(R.wz[e]));
 #pragma unroll
+    for (int jj = 0; jj < HW; ++jj) asm volatile("" : "+v"(R.wh[jj]));
+#pragma unroll
     for (int q = 0; q < NBC; ++q)
 #pragma unroll
       for (int e = 0; e < BW; ++e) asm volatile("" : "+v"(RB.wbc[q][e]));
@@ -313,6 +347,34 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       for (int q = 0; q < NBC; ++q)
 #pragma unroll
         for (int e = 0; e < KS; ++e) Buf::template unpack<1>(&RB.wbc[q][e], &rbc[q][e]);
+    }
+    if constexpr (CONV) {
+      // u_t = silu(bias + sum_j w4[j] x_{t-3+j}); the same stores on every
+      // tile (steps past L to the dropping offset, as in the epilogue)
+      float xs[V + 3];
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) {
+        float v;
+        Buf::template unpack<1>(&R.wh[jj], &v);
+        xs[jj] = t0 + pt - 3 + jj >= 0 ? v : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) xs[3 + e] = ru[e];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float pre = cbias;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pre = __builtin_fmaf(w4[jj], xs[e + jj], pre);
+        ru[e] = silu(pre);
+      }
+      const uint32_t toff = static_cast<uint32_t>(t0) * ES;
+      if constexpr (VEC) {
+        Buf::template st<V>(rUO, t0 + pt < Li ? poff + toff : kDropOffset, ru);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          Buf::template st<1>(rUO, t0 + pt + e < Li ? poff + toff + e * ES : kDropOffset, &ru[e]);
+      }
     }
     // whole tiles take no per-element masks; softplus is one uniform branch
     float dt[V], du[V];
@@ -523,7 +585,7 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
   }
 }
 
-template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS>
+template <typename IO, int S, int KS, bool GATED, bool VEC, bool CS, bool CONV>
 static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   using T = typename IO::T;
   constexpr int RS = kLpSeg * (KS + 4);
@@ -533,8 +595,11 @@ static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   g.Bg = static_cast<const T*>(a.B); g.Cg = static_cast<const T*>(a.C); g.Dg = a.D;
   g.zg = static_cast<const T*>(a.z); g.biasg = a.bias; g.yg = static_cast<T*>(a.y);
   g.last_state = a.last_state; g.h0 = a.h0; g.chunk_states = a.chunk_states;
+  g.convw = a.conv_w; g.convb = a.conv_b; g.uo = static_cast<T*>(a.u_out);
   LparSizes sz;
   sz.batch = a.batch; sz.dim = a.dim; sz.dstate = a.dstate; sz.L = a.L; sz.softplus = a.softplus;
+  sz.convk = CONV ? a.conv_k : 0;
+  if (CONV && (a.conv_w == nullptr || a.conv_k < 1 || a.conv_k > 4)) return hipErrorInvalidValue;
   const bool cs = a.chunk_states != nullptr && a.state_chunk > 0;
   if (cs && a.state_chunk % (2 * KS) != 0) return hipErrorInvalidValue;
   // a spacing of L or more has no boundary before step L; any multiple of 32
@@ -542,7 +607,7 @@ static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   sz.sc = cs ? static_cast<int>(a.state_chunk <= a.L ? a.state_chunk : (a.L / 32 + 1) * 32) : 0;
   sz.nsc = cs ? (a.L + a.state_chunk - 1) / a.state_chunk : 0;
   const dim3 grid(static_cast<unsigned>((a.dim + kLpCh - 1) / kLpCh), static_cast<unsigned>(a.batch));
-  auto kern = ssm_lpar_kernel<IO, S, KS, GATED, VEC, CS>;
+  auto kern = ssm_lpar_kernel<IO, S, KS, GATED, VEC, CS, CONV>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
@@ -550,21 +615,24 @@ static hipError_t launch_lpar_v(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename IO, bool CS>
+template <typename IO, bool CS, bool CONV>
 static hipError_t dispatch_lpar(const FwdArgs& a, hipStream_t st) {
   constexpr int S = kLparStates, KS = kLparSegSteps;
   const bool vec = a.L % 8 == 0;
   if (a.z != nullptr)
-    return vec ? launch_lpar_v<IO, S, KS, true, true, CS>(a, st) : launch_lpar_v<IO, S, KS, true, false, CS>(a, st);
-  return vec ? launch_lpar_v<IO, S, KS, false, true, CS>(a, st) : launch_lpar_v<IO, S, KS, false, false, CS>(a, st);
+    return vec ? launch_lpar_v<IO, S, KS, true, true, CS, CONV>(a, st)
+               : launch_lpar_v<IO, S, KS, true, false, CS, CONV>(a, st);
+  return vec ? launch_lpar_v<IO, S, KS, false, true, CS, CONV>(a, st)
+             : launch_lpar_v<IO, S, KS, false, false, CS, CONV>(a, st);
 }
 
 template <typename IO>
 static hipError_t dispatch_lpar(const FwdArgs& a, hipStream_t st) {
-  // the chunk-state stores and their per-tile mask are compiled in only where
-  // they are asked for
-  return a.chunk_states != nullptr && a.state_chunk > 0 ? dispatch_lpar<IO, true>(a, st)
-                                                        : dispatch_lpar<IO, false>(a, st);
+  // the chunk-state stores (and their per-tile mask) and the conv front are
+  // compiled in only where they are asked for
+  const bool cs = a.chunk_states != nullptr && a.state_chunk > 0;
+  if (a.conv_w != nullptr) return cs ? dispatch_lpar<IO, true, true>(a, st) : dispatch_lpar<IO, false, true>(a, st);
+  return cs ? dispatch_lpar<IO, true, false>(a, st) : dispatch_lpar<IO, false, false>(a, st);
 }
 
 hipError_t launch_lpar(const FwdArgs& a, bool bf16, hipStream_t st) {

@@ -141,21 +141,15 @@ def test_states_entry_point_rejects_bad_state_chunk():
     assert lib.ssm_scan_fwd_states(*args2, 64, 1, 64, 16, 256, 0, 0, None) == ssm.SSM_EINVAL
 
 
-def test_lpar_plan_rejects_conv():
-    """The L-parallel plan has no conv in front: forcing it with one is
-    SSM_EUNSUPPORTED, and a chunk-state spacing that is not a multiple of 32
-    stays SSM_EINVAL under it, both before any HIP call."""
+def test_lpar_plan_checks_state_chunk():
+    """Under the L-parallel plan a chunk-state spacing that is not a multiple
+    of 32 is SSM_EINVAL, and an unknown plan number stays invalid, both before
+    any HIP call."""
     lib = ssm.load_library()
     P = ctypes.c_void_p
     args = [P(BIG), P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, None, None, 0, None, P(6 * BIG),
             P(7 * BIG), P(8 * BIG)]
     assert lib.ssm_scan_fwd_states(*args, 48, 1, 64, 16, 256, 0, ssm.PLANS["lpar"], None) == ssm.SSM_EINVAL
-    # conv in front: x, conv_w, conv_b, K, delta, A, B, C, D, z, bias, softplus, h0, y, last, u_out, chunk_states
-    conv = [P(BIG), P(9 * BIG), None, 4, P(2 * BIG), P(3 * BIG), P(4 * BIG), P(5 * BIG), None, None, None, 0, None,
-            P(6 * BIG), P(7 * BIG), None, None, 0, 1, 64, 16, 256, 0]
-    assert lib.ssm_scan_fwd_conv(*conv, ssm.PLANS["lpar"], None) == ssm.SSM_EUNSUPPORTED
-    assert "L-parallel" in lib.ssm_last_error().decode()
-    # an unknown plan number stays invalid
     assert lib.ssm_scan_fwd_states(*args, 64, 1, 64, 16, 256, 0, 5, None) == ssm.SSM_EINVAL
 
 

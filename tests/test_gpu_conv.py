@@ -58,6 +58,10 @@ CASES = [
     (2, 24, 8, 77, 1, "carry"),
     (1, 16, 16, 5000, 4, "twopass"),
     (1, 20, 16, 3, 4, "carry"),
+    (2, 40, 16, 150, 4, "lpar"),
+    (1, 37, 16, 700, 3, "lpar"),
+    (2, 9, 5, 1029, 1, "lpar"),
+    (1, 64, 16, 2048, 4, "lpar"),
 ]
 
 
@@ -78,12 +82,13 @@ def test_conv_scan_matches_oracle(case, dtype):
     assert rel_err(_host(last), last_ref) <= 1e-4, "last_state"
 
 
-def test_conv_scan_states_and_no_u_output():
+@pytest.mark.parametrize("plan", ["auto", "lpar"])
+def test_conv_scan_states_and_no_u_output(plan):
     """h0, chunk-boundary states, no conv bias, no u output."""
     inp = make(2, 48, 16, 320, torch.float32, 4, seed=2, with_bias=False, with_h0=True)
     y, last, cs, u = ssm.ssm_scan_fwd_conv(inp["u"], inp["conv_w"], inp["delta"], inp["A"], inp["B"], inp["C"],
                                            D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], delta_softplus=True,
-                                           h0=inp["h0"], state_chunk=64)
+                                           h0=inp["h0"], state_chunk=64, plan=plan)
     torch.cuda.synchronize(DEV)
     assert u is None
     _, (y_ref, last_ref, bounds) = oracle(inp, state_chunk=64)

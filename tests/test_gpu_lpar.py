@@ -144,6 +144,34 @@ def test_lpar_chunk_states_feed_the_backward():
         assert rel_err(a, c) <= 1e-4, name
 
 
+def test_lpar_conv_chunk_states_feed_the_backward():
+    """With the conv in front: the conv backward from the L-parallel plan's
+    chunk states gives the gradients it gives from the carry plan's."""
+    inp = small_inputs(2, 24, 16, 1000, seed=84)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(85)
+    conv_w = torch.randn((24, 4), generator=g, device=DEV) * 0.25
+    conv_b = torch.randn((24,), generator=g, device=DEV) * 0.1
+    dy = torch.randn(inp["u"].shape, generator=g, device=DEV, dtype=inp["u"].dtype)
+    sc = 128
+    grads, ys = [], []
+    for plan in ("lpar", "carry"):
+        y, _, cs, _ = ssm.ssm_scan_fwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"],
+                                            conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                            delta_softplus=True, state_chunk=sc, plan=plan)
+        gr = ssm.ssm_scan_bwd_conv(inp["u"], conv_w, inp["delta"], inp["A"], inp["B"], inp["C"], cs, sc, dy,
+                                   conv_b=conv_b, D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                   delta_softplus=True)
+        grads.append(gr)
+        ys.append(y)
+    torch.cuda.synchronize(DEV)
+    assert rel_err(_host(ys[0]), _host(ys[1])) <= 1e-4
+    for name in grads[0]:
+        if grads[0][name] is None:
+            continue
+        assert rel_err(_host(grads[0][name]), _host(grads[1][name])) <= 1e-4, name
+
+
 def test_lpar_extreme_values():
     """delta over [-80, 80], A down to -400 (decays that underflow within a
     step, so segment products of exactly zero) and inputs of magnitude 1e3."""
