@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "78db5201d0aa6d9e", "plan": "mixed", "fetch_bytes": 333335907, "write_bytes": 101454433,
+    "130m": {"digest": "070b8d7d8d51d285", "plan": "mixed", "fetch_bytes": 333397264, "write_bytes": 101450766,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "78db5201d0aa6d9e", "plan": "carry", "fetch_bytes": 431252229, "write_bytes": 136562264,
+    "1.4b": {"digest": "070b8d7d8d51d285", "plan": "carry", "fetch_bytes": 430601807, "write_bytes": 136316297,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "78db5201d0aa6d9e", "plan": "lpar", "fetch_bytes": 1204720699, "write_bytes": 537001984,
+    "long": {"digest": "070b8d7d8d51d285", "plan": "lpar", "fetch_bytes": 1214826336, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "78db5201d0aa6d9e", "plan": "carry", "fetch_bytes": 5348522982, "write_bytes": 1349193828,
+    "varlen": {"digest": "070b8d7d8d51d285", "plan": "carry", "fetch_bytes": 4121367781, "write_bytes": 1349420608,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "78db5201d0aa6d9e", "plan": "mixed", "fetch_bytes": 335487307, "write_bytes": 101455943,
+    "130m+conv4": {"digest": "070b8d7d8d51d285", "plan": "mixed", "fetch_bytes": 336390237, "write_bytes": 101450354,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
@@ -194,9 +194,9 @@ MEASURED_DECODE_TRAFFIC = {
 # The same for the backward kernel (ssm_bwd.hip), keyed by workload and
 # conv taps, at the default state_chunk (128) and states per lane (auto).
 MEASURED_BWD_TRAFFIC = {
-    ("130m", 0): {"digest": "5f30772464e8dca0", "fetch_bytes": 518857647, "write_bytes": 564924096,
+    ("130m", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 518755437, "write_bytes": 564459744,
                   "profile": "profiles/ssm_bwd_kernel_130m_f32.md"},
-    ("1.4b", 0): {"digest": "5f30772464e8dca0", "fetch_bytes": 1123430770, "write_bytes": 1235154480,
+    ("1.4b", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 1285530811, "write_bytes": 1176955072,
                   "profile": "profiles/ssm_bwd_kernel_1.4b_bf16.md"},
 }
 
