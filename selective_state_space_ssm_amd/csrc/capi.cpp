@@ -117,7 +117,9 @@ void choose(int64_t batch, int64_t dim, int64_t dstate, int64_t L, int* plan, in
     if (K > L / kMinChunk) K = L / kMinChunk;
     if (K > kMaxChunks) K = kMaxChunks;
     if (K >= 2) {
-      chunk = ceil_div(ceil_div(L, K), 64) * 64;
+      // whole groups of four 32-step tiles: the bfloat16 one-wave kernels
+      // run their tiles four at a time (identity tiles fill a chunk up)
+      chunk = ceil_div(ceil_div(L, K), 128) * 128;
       pl = SSM_PLAN_TWOPASS;
       S = states_for(groups * ceil_div(L, chunk));
     }
