@@ -133,8 +133,10 @@ hipError_t launch_zero(const ZeroList& z, hipStream_t st);
 
 // L-parallel single-pass forward (ssm_lpar.hip): workgroups of 4 channels x
 // all states of one batch row; each tile is 16 segments of kLparSegSteps
-// steps, one per lane of a row of 16.  Takes u, delta, A, B, C, D, z, bias,
-// h0, y and last_state of `a` (no conv, no chunk states).
+// steps, one per lane of a row of 16.  Takes every field of `a` that the
+// carry plan takes: u (or x with the conv), delta, A, B, C, D, z, bias, h0,
+// y, last_state, chunk_states / state_chunk (a multiple of 32) and the conv
+// front (conv_w, conv_b, conv_k, u_out).
 constexpr int kLparStates = 4;     // states per lane (16/kLparStates wavefronts)
 constexpr int kLparSegSteps = 16;
 hipError_t launch_lpar(const FwdArgs& a, bool bf16, hipStream_t st);
