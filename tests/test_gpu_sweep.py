@@ -21,7 +21,7 @@ from oracle import cpu, ref
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-PLANS = ("auto", "carry", "mixed", "twopass")
+PLANS = ("auto", "carry", "mixed", "twopass", "lpar")
 
 
 def rel_err(got, want):
