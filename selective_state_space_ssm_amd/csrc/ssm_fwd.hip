@@ -754,7 +754,27 @@ __global__ __launch_bounds__(256, 2) void ssm_mixed_kernel(RowArgs<IO> args, CsS
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nA = p.batch * m.pairs;
-  const int64_t x = blockIdx.x;
+  int64_t x = blockIdx.x;
+  if (gridDim.z == 1) {
+    // XCD-contiguous ranges within each kind of block (the two-group blocks
+    // are dispatched first, then the one-group blocks): an XCD then works on
+    // whole batch rows, whose B and C stay in its L2, and still gets as many
+    // blocks of each kind as the others
+    const int64_t nB = p.batch * m.singles;
+    const int64_t xcd = x % 8;
+    if (x < nA) {
+      const int64_t q = nA / 8, r = nA % 8;
+      x = xcd * q + (xcd < r ? xcd : r) + x / 8;
+    } else {
+      const int64_t first = nA + (xcd - nA % 8 + 8) % 8;
+      int64_t off = 0;
+      for (int64_t xx = 0; xx < xcd; ++xx) {
+        const int64_t o = (xx - nA % 8 + 8) % 8;
+        off += o < nB ? (nB - o + 7) / 8 : 0;
+      }
+      x = nA + off + (x - first) / 8;
+    }
+  }
   if (x < nA) {
     const int sub = wave >> 1;
     const int64_t b = x / m.pairs;
