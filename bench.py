@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "070b8d7d8d51d285", "plan": "mixed", "fetch_bytes": 333397264, "write_bytes": 101450766,
+    "130m": {"digest": "544fac74413b3577", "plan": "mixed", "fetch_bytes": 318713151, "write_bytes": 101450072,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "070b8d7d8d51d285", "plan": "carry", "fetch_bytes": 430601807, "write_bytes": 136316297,
+    "1.4b": {"digest": "544fac74413b3577", "plan": "carry", "fetch_bytes": 430645070, "write_bytes": 136316264,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "070b8d7d8d51d285", "plan": "lpar", "fetch_bytes": 1214826336, "write_bytes": 537001984,
+    "long": {"digest": "544fac74413b3577", "plan": "lpar", "fetch_bytes": 1214419357, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "070b8d7d8d51d285", "plan": "carry", "fetch_bytes": 4121367781, "write_bytes": 1349420608,
+    "varlen": {"digest": "544fac74413b3577", "plan": "carry", "fetch_bytes": 4121016893, "write_bytes": 1347876793,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "070b8d7d8d51d285", "plan": "mixed", "fetch_bytes": 336390237, "write_bytes": 101450354,
+    "130m+conv4": {"digest": "544fac74413b3577", "plan": "mixed", "fetch_bytes": 320480883, "write_bytes": 101449932,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
