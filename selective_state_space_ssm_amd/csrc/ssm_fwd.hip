@@ -331,6 +331,15 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   // next tile's load in another register and wait for it at the loop's end.
   float nDu[V], nG[V];
   float cDu[V], cG[V];
+  // Identity tiles (one-wave groups, full pass): a tile whose Delta2 and
+  // Delta*u are all exactly zero and whose B is finite leaves every state
+  // unchanged (a = exp2(0) = 1, b = 0 * B = 0), so its recurrence reduces to
+  // the partial sums C.h.  Prep decides it for the tile it prepares (one OR
+  // per step over the bits of Delta2 and Delta*u, a wave vote, and only when
+  // that vote says zero the finiteness of B); the recurrence takes it from
+  // cur_live.  Varlen padding (Delta = 0 past each length) makes such tiles.
+  constexpr bool kSkip = (W == 1) && MODE == kFull && !CONV;
+  bool next_live = true, cur_live = true;
 
   // ---- prep: Delta2, Delta*u, B, C of the tile held in registers into LDS.
   // In the ragged last tile, steps past the chunk become identity steps
@@ -437,6 +446,27 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
         *reinterpret_cast<float4*>(sBC + bc_slot(q)) = v;
       }
     }
+    if constexpr (kSkip) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc |= __float_as_uint(dt[e]) | __float_as_uint(du[e]);
+      bool live = __builtin_amdgcn_ballot_w64((acc & 0x7fffffffu) != 0u) != 0u;
+      if (!live) {
+        // 0 * B is zero for a finite B and NaN otherwise (the loaded words
+        // past the chunk end can only make a tile live, which is always safe)
+        float zb = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BCQ; ++i) {
+          if (bcis_c[i]) continue;
+          zb = __builtin_fmaf(rbc[i].x, 0.0f, zb);
+          zb = __builtin_fmaf(rbc[i].y, 0.0f, zb);
+          zb = __builtin_fmaf(rbc[i].z, 0.0f, zb);
+          zb = __builtin_fmaf(rbc[i].w, 0.0f, zb);
+        }
+        live = __builtin_amdgcn_ballot_w64((__float_as_uint(zb) & 0x7fffffffu) != 0u) != 0u;
+      }
+      next_live = live;
+    }
   };
 
   // ---- recurrence of one tile from LDS
@@ -480,6 +510,28 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       __builtin_amdgcn_sched_barrier(0);
     } else {
       read_bc();
+    }
+    if (kSkip && !cur_live) {
+      // identity tile: the states stay; only the partial sums C.h
+      static_for<0, 2>([&](auto HH) {
+        constexpr int hh = decltype(HH)::value;
+        float y4[4];
+        static_for<0, 16>([&](auto JJ) {
+          constexpr int j = decltype(JJ)::value;
+          float yv = 0.0f;
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            if (s == 0)
+              yv = mul_bcast16<j>(cc[s][hh], h[s]);
+            else
+              fmac_bcast16<j>(yv, cc[s][hh], h[s]);
+          }
+          y4[j % 4] = yv;
+          if (j % 4 == 3)
+            *reinterpret_cast<float4*>(rowP + 16 * hh + j - 3) = make_float4(y4[0], y4[1], y4[2], y4[3]);
+        });
+      });
+      return;
     }
     static_for<0, 2>([&](auto HH) {
       constexpr int hh = decltype(HH)::value;
@@ -612,6 +664,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     cDu[e] = nDu[e];
     cG[e] = nG[e];
   }
+  cur_live = next_live;
   if constexpr (!kPairLoads) load_tile(A, t_begin + 2 * kTT);
   // A one-wave workgroup needs no barrier: its LDS accesses run in program
   // order.
@@ -657,6 +710,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       cDu[e] = nDu[e];
       cG[e] = nG[e];
     }
+    cur_live = next_live;
     loads();
     if constexpr (!kPre) __syncthreads();
   };
