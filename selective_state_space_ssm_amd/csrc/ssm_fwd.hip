@@ -338,8 +338,17 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
   // per step over the bits of Delta2 and Delta*u, a wave vote, and only when
   // that vote says zero the finiteness of B); the recurrence takes it from
   // cur_live.  Varlen padding (Delta = 0 past each length) makes such tiles.
+  // A must be finite as well (checked once).
   constexpr bool kSkip = (W == 1) && MODE == kFull && !CONV;
   bool next_live = true, cur_live = true;
+  // a non-finite A makes exp2(0 * A) NaN: such a group never skips
+  bool a_finite = true;
+  if constexpr (kSkip) {
+    float za = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) za = __builtin_fmaf(An[s], 0.0f, za);
+    a_finite = __builtin_amdgcn_ballot_w64((__float_as_uint(za) & 0x7fffffffu) != 0u) == 0u;
+  }
 
   // ---- prep: Delta2, Delta*u, B, C of the tile held in registers into LDS.
   // In the ragged last tile, steps past the chunk become identity steps
@@ -450,7 +459,7 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
       uint32_t acc = 0u;
 #pragma unroll
       for (int e = 0; e < V; ++e) acc |= __float_as_uint(dt[e]) | __float_as_uint(du[e]);
-      bool live = __builtin_amdgcn_ballot_w64((acc & 0x7fffffffu) != 0u) != 0u;
+      bool live = !a_finite || __builtin_amdgcn_ballot_w64((acc & 0x7fffffffu) != 0u) != 0u;
       if (!live) {
         // 0 * B is zero for a finite B and NaN otherwise (the loaded words
         // past the chunk end can only make a tile live, which is always safe)
