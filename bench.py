@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "f706474e5dfbbfa0", "plan": "mixed", "fetch_bytes": 318727397, "write_bytes": 101449884,
+    "130m": {"digest": "0ab8e7479b1cc478", "plan": "mixed", "fetch_bytes": 318727397, "write_bytes": 101449884,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "f706474e5dfbbfa0", "plan": "carry", "fetch_bytes": 430494078, "write_bytes": 136315228,
+    "1.4b": {"digest": "0ab8e7479b1cc478", "plan": "carry", "fetch_bytes": 430494078, "write_bytes": 136315228,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "f706474e5dfbbfa0", "plan": "lpar", "fetch_bytes": 1213899129, "write_bytes": 537001984,
+    "long": {"digest": "0ab8e7479b1cc478", "plan": "lpar", "fetch_bytes": 1213899129, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "f706474e5dfbbfa0", "plan": "carry", "fetch_bytes": 4127520361, "write_bytes": 1347933340,
+    "varlen": {"digest": "0ab8e7479b1cc478", "plan": "carry", "fetch_bytes": 4127520361, "write_bytes": 1347933340,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "f706474e5dfbbfa0", "plan": "mixed", "fetch_bytes": 320499973, "write_bytes": 101449792,
+    "130m+conv4": {"digest": "0ab8e7479b1cc478", "plan": "mixed", "fetch_bytes": 320499973, "write_bytes": 101449792,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 

@@ -33,9 +33,12 @@
 //         sums + D*u, times silu(z); rounded to the storage type, stored.
 //   prep  (every thread, V steps of one channel, next tile): Delta2 =
 //         softplus(delta + bias) in log2 units and Delta*u into LDS; B and C
-//         of the tile (float32) into LDS.  The global loads of the tile
-//         after are issued right after, so they have a whole tile of
-//         recurrence to arrive.
+//         of the tile (float32) into LDS.  The global loads run two tiles
+//         ahead in two register sets (bfloat16 one-wave groups: four sets,
+//         a 128-byte line's two halves loaded together), issued after the
+//         epilogue.  One-wave groups also vote on whether the tile is an
+//         identity tile (all Delta2 and Delta*u zero, B finite), whose
+//         recurrence then reduces to the partial sums.
 // Exp is v_exp_f32 (2^x): A is used unscaled because Delta is kept as
 // Delta2 = Delta*log2(e); Delta*u is formed from Delta2*ln(2).
 //
