@@ -168,25 +168,25 @@ MEASURED_TRAFFIC = {
 
 # The same for the bare affine scan (affine_scan.hip), keyed by workload.
 MEASURED_AFFINE_TRAFFIC = {
-    "130m": {"digest": "fb9d6e51286ff07f", "fetch_bytes": 3221436849, "write_bytes": 3227328896,
+    "130m": {"digest": "fb9d6e51286ff07f", "fetch_bytes": 3221650903, "write_bytes": 3227796800,
              "profile": "profiles/affine_scan_kernel_130m_chains.md"},
 }
 
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "0a6fb3443f0d4a3c", "fetch_bytes": 187281295, "write_bytes": 50341856,
+    "130m": {"digest": "2cc35320918a04ad", "fetch_bytes": 187407557, "write_bytes": 50340848,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
-    "1.4b": {"digest": "0a6fb3443f0d4a3c", "fetch_bytes": 403034661, "write_bytes": 70321720,
+    "1.4b": {"digest": "2cc35320918a04ad", "fetch_bytes": 402997592, "write_bytes": 70898296,
              "profile": "profiles/ssm_proj_dma_kernel_out_proj_1.4b_bf16.md"},
 }
 
 
 # The same for the decode step (ssm_step.hip), keyed by workload and conv taps.
 MEASURED_DECODE_TRAFFIC = {
-    ("1.4b", 1024, 0): {"digest": "fab200ff92f6bbae", "fetch_bytes": 294450483, "write_bytes": 276824064,
+    ("1.4b", 1024, 0): {"digest": "f925c39ce5e23800", "fetch_bytes": 294450175, "write_bytes": 276824078,
                         "profile": "profiles/ssm_step_kernel_decode1024_1.4b_bf16.md"},
-    ("1.4b", 1024, 4): {"digest": "fab200ff92f6bbae", "fetch_bytes": 344916801, "write_bytes": 327155739,
+    ("1.4b", 1024, 4): {"digest": "f925c39ce5e23800", "fetch_bytes": 344918560, "write_bytes": 327155785,
                         "profile": "profiles/ssm_step_kernel_decode1024_conv4_1.4b_bf16.md"},
 }
 
@@ -194,9 +194,9 @@ MEASURED_DECODE_TRAFFIC = {
 # The same for the backward kernel (ssm_bwd.hip), keyed by workload and
 # conv taps, at the default state_chunk (128) and states per lane (auto).
 MEASURED_BWD_TRAFFIC = {
-    ("130m", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 518755437, "write_bytes": 564459744,
+    ("130m", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 518547702, "write_bytes": 550702720,
                   "profile": "profiles/ssm_bwd_kernel_130m_f32.md"},
-    ("1.4b", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 1285530811, "write_bytes": 1176955072,
+    ("1.4b", 0): {"digest": "1754b9904eacadfa", "fetch_bytes": 1269332303, "write_bytes": 1180293192,
                   "profile": "profiles/ssm_bwd_kernel_1.4b_bf16.md"},
 }
 
@@ -302,7 +302,7 @@ def decode_bench(args):
         for _ in range(max(1, args.warmup // per_run)):
             run()
         torch.cuda.synchronize(dev)
-    prewarm(run, dev, args.prewarm)
+    pw_s, pw_n = prewarm(run, dev, args.prewarm)
     nrun = max(1, args.steps // per_run)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -322,7 +322,8 @@ def decode_bench(args):
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     res = {"metric": "selective-scan decode step GB/s (state read + write + step inputs/outputs)",
            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": nrun * per_run,
-           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "prewarm": {"seconds": round(pw_s, 3), "launches": pw_n},
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)",
            "data": "synthetic (seeded; the workload's value recipes, one step)",
            "config": {"workload": w0.name + "-decode", "batch": w.batch, "d_inner": w.dim,
@@ -480,7 +481,7 @@ def bwd_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev, args.prewarm)
+    pw_s, pw_n = prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -496,6 +497,7 @@ def bwd_bench(args):
     out = {
         "metric": "selective-scan bwd GB/s (algorithmic bytes of the gradients pass); Gsteps.ch.state/s",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "prewarm": {"seconds": round(pw_s, 3), "launches": pw_n},
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 storage)",
         "data": "synthetic (seeded; shapes and value recipes of the workload)",
@@ -565,7 +567,7 @@ def affine_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev, args.prewarm)
+    pw_s, pw_n = prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -578,7 +580,8 @@ def affine_bench(args):
     bytes_alg = 16 * rows * L                    # a, b read; out_a, out_b written; float32
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     res = {"metric": "affine_scan GB/s (a, b in; products and states out)", "value": round(gbs, 2),
-           "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 5),
+           "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+           "prewarm": {"seconds": round(pw_s, 3), "launches": pw_n}, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic (seeded: a ~ U(0,1), b ~ N(0,1))",
            "config": {"workload": w.name + "-affine", "rows": rows, "seq_len": L},
@@ -641,7 +644,7 @@ def proj_bench(args):
     for _ in range(warm):
         step()
     torch.cuda.synchronize(dev)
-    prewarm(step, dev, args.prewarm)
+    pw_s, pw_n = prewarm(step, dev, args.prewarm)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -664,6 +667,7 @@ def proj_bench(args):
         "metric": ("output projection backward TFLOP/s (dy and dW: 4 b L d_model d_inner per step)" if args.bwd
                    else "output projection TFLOP/s (2 b L d_model d_inner per launch)"),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "prewarm": {"seconds": round(pw_s, 3), "launches": pw_n},
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16 (f32 accumulation)",
         "data": "synthetic (seeded: y ~ N(0,1), W ~ N(0,1)/sqrt(d_inner))",
