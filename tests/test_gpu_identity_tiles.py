@@ -74,3 +74,34 @@ def test_infinite_A_with_padding():
     inp["A"] = A.contiguous()
     y_ref, _ = check(inp)
     assert np.isnan(y_ref[0, 7, PAD:]).all() and not np.isnan(y_ref[1, 7]).any()
+
+
+def _pad_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        b = int(rng.integers(1, 5))
+        L = int(rng.integers(32, 3000))
+        out.append(dict(b=b, d=int(rng.integers(1, 70)), n=int(rng.integers(1, 17)), L=L,
+                        dtype=(torch.float32, torch.bfloat16)[int(rng.integers(2))],
+                        gated=bool(rng.integers(2)), with_D=bool(rng.integers(2)), with_bias=bool(rng.integers(2)),
+                        lens=[int(x) for x in rng.integers(0, L + 1, size=b)], seed=int(rng.integers(1 << 20))))
+    return out
+
+
+PADS = _pad_cases(8801, 16)
+
+
+@pytest.mark.parametrize("c", PADS, ids=lambda c: f"b{c['b']}d{c['d']}n{c['n']}L{c['L']}"
+                         f"{'-bf16' if c['dtype'] == torch.bfloat16 else ''}")
+def test_padded_rows_seeded_sweep(c):
+    """Random sizes and a random length per batch row (delta = -inf past it,
+    lengths from 0 to L), through the four-states-per-lane carry plan:
+    every element against the float64 oracle."""
+    inp = small_inputs(c["b"], c["d"], c["n"], c["L"], dtype=c["dtype"], gated=c["gated"], with_D=c["with_D"],
+                       with_bias=c["with_bias"], seed=c["seed"])
+    delta = inp["delta"].clone()
+    for bi, ln in enumerate(c["lens"]):
+        delta[bi, :, ln:] = float("-inf")
+    inp["delta"] = delta.contiguous()
+    check(inp)
