@@ -115,6 +115,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 using Rsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 family: 32-bit untyped data format
 
+// Cache policy of a buffer access (the AUX argument of ldw / st): kCacheNT
+// marks it non-temporal, for data read or written once that other
+// workgroups do not share (gfx950's nt bit).
+constexpr int kCacheNT = 2;
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRsrcWord3);
@@ -124,17 +129,17 @@ struct BufF32 {
   // raw 32-bit words of V elements, and their conversion to float32
   template <int V>
   static constexpr int kWords = V;
-  template <int V>
+  template <int V, int AUX = 0>
   static __device__ __forceinline__ void ldw(Rsrc r, uint32_t off, uint32_t* w) {
     if constexpr (V == 1) {
-      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
     } else if constexpr (V == 2) {
-      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
       w[0] = x.x; w[1] = x.y;
     } else {
 #pragma unroll
       for (int i = 0; i < V; i += 4) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, AUX);
         w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
       }
     }
@@ -160,21 +165,21 @@ struct BufF32 {
       }
     }
   }
-  template <int V>
+  template <int V, int AUX = 0>
   static __device__ __forceinline__ void st(Rsrc r, uint32_t off, const float* v) {
     if constexpr (V == 1) {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, AUX);
     } else if constexpr (V == 2) {
       u32x2 w;
       w.x = __float_as_uint(v[0]); w.y = __float_as_uint(v[1]);
-      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, AUX);
     } else {
 #pragma unroll
       for (int i = 0; i < V; i += 4) {
         u32x4 w;
         w.x = __float_as_uint(v[i]); w.y = __float_as_uint(v[i + 1]);
         w.z = __float_as_uint(v[i + 2]); w.w = __float_as_uint(v[i + 3]);
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + 4 * i, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + 4 * i, 0, AUX);
       }
     }
   }
@@ -183,17 +188,17 @@ struct BufF32 {
 struct BufBF16 {
   template <int V>
   static constexpr int kWords = (V + 1) / 2;
-  template <int V>
+  template <int V, int AUX = 0>
   static __device__ __forceinline__ void ldw(Rsrc r, uint32_t off, uint32_t* w) {
     if constexpr (V == 1) {
-      w[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16;
+      w[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX)) << 16;
     } else if constexpr (V == 2) {
-      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
     } else if constexpr (V == 4) {
-      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
       w[0] = x.x; w[1] = x.y;
     } else {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
       w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
   }
@@ -226,24 +231,24 @@ struct BufBF16 {
       o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
     }
   }
-  template <int V>
+  template <int V, int AUX = 0>
   static __device__ __forceinline__ void st(Rsrc r, uint32_t off, const float* v) {
     if constexpr (V == 1) {
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(BF16::cvt(v[0])), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(BF16::cvt(v[0])), r, off, 0, AUX);
     } else if constexpr (V == 2) {
-      __builtin_amdgcn_raw_buffer_store_b32(BF16::cvt2(v[0], v[1]), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(BF16::cvt2(v[0], v[1]), r, off, 0, AUX);
     } else if constexpr (V == 4) {
       u32x2 w;
       w.x = BF16::cvt2(v[0], v[1]);
       w.y = BF16::cvt2(v[2], v[3]);
-      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, AUX);
     } else {
       u32x4 w;
       w.x = BF16::cvt2(v[0], v[1]);
       w.y = BF16::cvt2(v[2], v[3]);
       w.z = BF16::cvt2(v[4], v[5]);
       w.w = BF16::cvt2(v[6], v[7]);
-      __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, AUX);
     }
   }
 };

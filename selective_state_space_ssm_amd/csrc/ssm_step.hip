@@ -42,6 +42,8 @@ struct BF16S {
   }
 };
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 // quad_perm DPP controls: swap neighbours, swap pairs
 constexpr int kQuadSwap1 = 0xB1;  // [1, 0, 3, 2]
 constexpr int kQuadSwap2 = 0x4E;  // [2, 3, 0, 1]
@@ -118,7 +120,9 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
   float h[4], bv[4], cv[4], av[4];
   if (has_states) {
     if constexpr (VEC4) {
-      const float4 hs = *reinterpret_cast<const float4*>(a.state_in + so);
+      // the state is read and written once per step: non-temporal
+      const f32x4v hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(a.state_in + so));
+      const float4 hs = make_float4(hv[0], hv[1], hv[2], hv[3]);
       const float4 as = *reinterpret_cast<const float4*>(a.A + d * N + n0);
       h[0] = hs.x; h[1] = hs.y; h[2] = hs.z; h[3] = hs.w;
       av[0] = as.x; av[1] = as.y; av[2] = as.z; av[3] = as.w;
@@ -188,7 +192,8 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepDev<IO> a) {
       part = __builtin_fmaf(cv[e], h[e], part);
     }
     if constexpr (VEC4) {
-      *reinterpret_cast<float4*>(a.state_out + so) = make_float4(h[0], h[1], h[2], h[3]);
+      const f32x4v hw = {h[0], h[1], h[2], h[3]};
+      __builtin_nontemporal_store(hw, reinterpret_cast<f32x4v*>(a.state_out + so));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
