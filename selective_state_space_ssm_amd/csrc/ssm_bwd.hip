@@ -326,10 +326,10 @@ __global__ __launch_bounds__(256 / S, S == 1 ? 3 : 2) void ssm_bwd_kernel(BwdDev
     constexpr bool FULL = decltype(full_c)::value;
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
     if constexpr (CONV) {
-      // before step 0 of channel 0 the offset wraps past the resource and
-      // reads zero; the conv front zeroes the other steps before 0
+      // x at steps pt-3 .. pt-1 (halo_offset: never below zero; the conv
+      // front zeroes the steps before 0)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) Buf::template ldw<1>(rU, poff + toff - (3 - j) * ES, &R.wh[j]);
+      for (int j = 0; j < 3; ++j) Buf::template ldw<1>(rU, halo_offset(poff + toff, (3 - j) * ES), &R.wh[j]);
     }
     if constexpr (VEC) {
       Buf::template ldw<V>(rU, poff + toff, R.wu);

@@ -120,6 +120,17 @@ constexpr int kRsrcWord3 = 0x00020000;  // gfx9 family: 32-bit untyped data form
 // workgroups do not share (gfx950's nt bit).
 constexpr int kCacheNT = 2;
 
+// Byte offset `back` bytes before offset `off`, saturated at zero (one
+// v_sub_u32 with clamp).  For the conv halo: a slot before the start of
+// the buffer then reads word 0, whose value the caller discards (the step
+// is before 0).  A wrapped offset would not be safe: the compiler may
+// merge the halo with the neighbouring loads and address those as the
+// wrapped base plus an immediate, and the range check does not wrap, so
+// they would read zero.
+__device__ __forceinline__ uint32_t halo_offset(uint32_t off, uint32_t back) {
+  return __builtin_elementwise_sub_sat(off, back);
+}
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRsrcWord3);

@@ -253,10 +253,10 @@ __device__ __forceinline__ void rows_group(const RowArgs<IO>& args, const CsSize
     }
     const uint32_t toff = static_cast<uint32_t>(t0) * ES;
     if constexpr (CONV) {
-      // x at steps pt-3 .. pt-1 of the tile (before step 0 of channel 0 the
-      // offset wraps past the resource and reads zero; prep zeroes the rest)
+      // x at steps pt-3 .. pt-1 of the tile (halo_offset: never below zero;
+      // prep zeroes the steps before 0)
 #pragma unroll
-      for (int j = 0; j < HW; ++j) Buf::template ldw<1>(rU, poff + toff - (HW - j) * ES, &R.wh[j]);
+      for (int j = 0; j < HW; ++j) Buf::template ldw<1>(rU, halo_offset(poff + toff, (HW - j) * ES), &R.wh[j]);
     }
     if constexpr (VEC) {
       Buf::template ldw<V, kNT>(rU, poff + toff, wu);

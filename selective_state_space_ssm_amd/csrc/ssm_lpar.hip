@@ -281,10 +281,10 @@ __global__ __launch_bounds__(1024 / S, 2) void ssm_lpar_kernel(LparArgs<IO> args
       for (int e = 0; e < RW; ++e) R.wz[e] = 0u;
     }
     if constexpr (CONV) {
-      // before step 0 of the first channel the offset wraps past the
-      // resource and reads zero; prep zeroes the other rows' tails
+      // x at steps pt-3 .. pt-1 (halo_offset: never below zero; prep
+      // zeroes the steps before 0)
 #pragma unroll
-      for (int jj = 0; jj < 3; ++jj) Buf::template ldw<1>(rU, poff + toff - (3 - jj) * ES, &R.wh[jj]);
+      for (int jj = 0; jj < 3; ++jj) Buf::template ldw<1>(rU, halo_offset(poff + toff, (3 - jj) * ES), &R.wh[jj]);
     } else {
       R.wh[0] = 0u;
     }
