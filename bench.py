@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "1eca81fad724fe6c", "plan": "mixed", "fetch_bytes": 314244178, "write_bytes": 101449740,
+    "130m": {"digest": "6f7f3370409d5913", "plan": "mixed", "fetch_bytes": 314431935, "write_bytes": 101449752,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "1eca81fad724fe6c", "plan": "carry", "fetch_bytes": 430513140, "write_bytes": 136315008,
+    "1.4b": {"digest": "6f7f3370409d5913", "plan": "carry", "fetch_bytes": 430501118, "write_bytes": 136315745,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "1eca81fad724fe6c", "plan": "lpar", "fetch_bytes": 1213615307, "write_bytes": 537001984,
+    "long": {"digest": "6f7f3370409d5913", "plan": "lpar", "fetch_bytes": 1214098368, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "1eca81fad724fe6c", "plan": "carry", "fetch_bytes": 4127252819, "write_bytes": 1347971992,
+    "varlen": {"digest": "6f7f3370409d5913", "plan": "carry", "fetch_bytes": 4127798542, "write_bytes": 1347960280,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "1eca81fad724fe6c", "plan": "mixed", "fetch_bytes": 320500129, "write_bytes": 101449745,
+    "130m+conv4": {"digest": "6f7f3370409d5913", "plan": "mixed", "fetch_bytes": 320503286, "write_bytes": 101449730,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
@@ -175,18 +175,18 @@ MEASURED_AFFINE_TRAFFIC = {
 
 # The same for the output projection kernel (ssm_proj.hip).
 MEASURED_PROJ_TRAFFIC = {
-    "130m": {"digest": "43ce8252d6fa44c4", "fetch_bytes": 187258280, "write_bytes": 50338896,
+    "130m": {"digest": "bbc4ecdf63ff7a67", "fetch_bytes": 187462755, "write_bytes": 50341984,
              "profile": "profiles/ssm_proj_gemm_kernel_out_proj_130m_f32.md"},
-    "1.4b": {"digest": "43ce8252d6fa44c4", "fetch_bytes": 402997880, "write_bytes": 69850816,
+    "1.4b": {"digest": "bbc4ecdf63ff7a67", "fetch_bytes": 402999512, "write_bytes": 71230864,
              "profile": "profiles/ssm_proj_dma_kernel_out_proj_1.4b_bf16.md"},
 }
 
 
 # The same for the decode step (ssm_step.hip), keyed by workload and conv taps.
 MEASURED_DECODE_TRAFFIC = {
-    ("1.4b", 1024, 0): {"digest": "6336de353aac6245", "fetch_bytes": 294450084, "write_bytes": 276872521,
+    ("1.4b", 1024, 0): {"digest": "6336de353aac6245", "fetch_bytes": 294450084, "write_bytes": 276934839,
                         "profile": "profiles/ssm_step_kernel_decode1024_1.4b_bf16.md"},
-    ("1.4b", 1024, 4): {"digest": "6336de353aac6245", "fetch_bytes": 344886085, "write_bytes": 327160654,
+    ("1.4b", 1024, 4): {"digest": "6336de353aac6245", "fetch_bytes": 344886085, "write_bytes": 327182103,
                         "profile": "profiles/ssm_step_kernel_decode1024_conv4_1.4b_bf16.md"},
 }
 
@@ -194,9 +194,9 @@ MEASURED_DECODE_TRAFFIC = {
 # The same for the backward kernel (ssm_bwd.hip), keyed by workload and
 # conv taps, at the default state_chunk (128) and states per lane (auto).
 MEASURED_BWD_TRAFFIC = {
-    ("130m", 0): {"digest": "0be2a8fcf04cb254", "fetch_bytes": 487365386, "write_bytes": 556220144,
+    ("130m", 0): {"digest": "78e6d6e7f03b0b62", "fetch_bytes": 519179880, "write_bytes": 563931584,
                   "profile": "profiles/ssm_bwd_kernel_130m_f32.md"},
-    ("1.4b", 0): {"digest": "0be2a8fcf04cb254", "fetch_bytes": 1285975934, "write_bytes": 1173213576,
+    ("1.4b", 0): {"digest": "78e6d6e7f03b0b62", "fetch_bytes": 1289531535, "write_bytes": 1178266904,
                   "profile": "profiles/ssm_bwd_kernel_1.4b_bf16.md"},
 }
 
