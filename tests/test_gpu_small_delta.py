@@ -116,7 +116,7 @@ def test_decode_steps(dtype):
     state = torch.zeros((3, 70, 16), device=DEV)
     ys = []
     for t in range(32):
-        pick = lambda x: x[..., t].contiguous()
+        pick = lambda x: x[..., t].clone(memory_format=torch.contiguous_format)
         y, state = ssm.ssm_step(pick(inp["u"]), pick(inp["delta"]), inp["A"], pick(inp["B"]), pick(inp["C"]), state,
                                 delta_bias=inp["delta_bias"], delta_softplus=True)
         ys.append(y)

@@ -45,7 +45,7 @@ def seq_inputs(b, d, n, L, dtype, seed, gated=True, with_D=True, with_bias=True)
 
 
 def step_at(inp, t, state, softplus=True, state_out=None):
-    pick = lambda x: None if x is None else x[..., t].contiguous()
+    pick = lambda x: None if x is None else x[..., t].clone(memory_format=torch.contiguous_format)
     return ssm.ssm_step(pick(inp["u"]), pick(inp["delta"]), inp["A"], pick(inp["B"]), pick(inp["C"]), state,
                         D=inp["D"], z=pick(inp["z"]), delta_bias=inp["delta_bias"], delta_softplus=softplus,
                         state_out=state_out)
@@ -133,7 +133,7 @@ def test_step_conv_sequence_matches_conv_scan(K, inplace, dtype):
     state = torch.zeros((b, d, n), device=DEV)
     ys, us = [], []
     for t in range(T):
-        pick = lambda x: None if x is None else x[..., t].contiguous()
+        pick = lambda x: None if x is None else x[..., t].clone(memory_format=torch.contiguous_format)
         kw = dict(conv_b=conv_b, D=inp["D"], z=pick(inp["z"]), delta_bias=inp["delta_bias"], delta_softplus=True,
                   return_u=True)
         if not inplace:
@@ -170,7 +170,7 @@ def test_step_conv_matches_conv_forward_on_gpu():
     cs = torch.zeros((b, d, 3), device=DEV)
     state = torch.zeros((b, d, n), device=DEV)
     for t in range(T):
-        pick = lambda x: x[..., t].contiguous()
+        pick = lambda x: x[..., t].clone(memory_format=torch.contiguous_format)
         y, cs, state, _ = ssm.ssm_step_conv(pick(inp["u"]), conv_w, cs, pick(inp["delta"]), inp["A"], pick(inp["B"]),
                                             pick(inp["C"]), state, D=inp["D"], z=pick(inp["z"]),
                                             delta_bias=inp["delta_bias"], delta_softplus=True)

@@ -253,7 +253,7 @@ def test_decode_sweep(c):
     cstate = torch.zeros((c["b"], c["d"], K - 1), device=DEV) if K > 1 else None
     ys = []
     for t in range(T):
-        pick = lambda v: None if v is None else v[..., t].contiguous()
+        pick = lambda v: None if v is None else v[..., t].clone(memory_format=torch.contiguous_format)
         if K:
             y, cstate, state, _ = ssm.ssm_step_conv(pick(inp["u"]), conv_w, cstate, pick(inp["delta"]), inp["A"],
                                                     pick(inp["B"]), pick(inp["C"]), state, conv_b=conv_b,
