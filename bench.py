@@ -154,15 +154,15 @@ COPY_BYTES = 1 << 30   # bytes read (and written) by one launch of the calibrati
 # and it is reported as null).  Each entry names the profile summary the
 # counts come from.
 MEASURED_TRAFFIC = {
-    "130m": {"digest": "6f7f3370409d5913", "plan": "mixed", "fetch_bytes": 314431935, "write_bytes": 101449752,
+    "130m": {"digest": "185b0e45f1e5c5cc", "plan": "mixed", "fetch_bytes": 314439952, "write_bytes": 101449761,
              "profile": "profiles/ssm_mixed_kernel_130m_f32.md"},
-    "1.4b": {"digest": "6f7f3370409d5913", "plan": "carry", "fetch_bytes": 430501118, "write_bytes": 136315745,
+    "1.4b": {"digest": "185b0e45f1e5c5cc", "plan": "carry", "fetch_bytes": 430509561, "write_bytes": 136315840,
              "profile": "profiles/ssm_rows_kernel_1.4b_bf16.md"},
-    "long": {"digest": "6f7f3370409d5913", "plan": "lpar", "fetch_bytes": 1214098368, "write_bytes": 537001984,
+    "long": {"digest": "185b0e45f1e5c5cc", "plan": "lpar", "fetch_bytes": 1167081322, "write_bytes": 537001984,
              "profile": "profiles/ssm_lpar_kernel_long_f32.md"},
-    "varlen": {"digest": "6f7f3370409d5913", "plan": "carry", "fetch_bytes": 4127798542, "write_bytes": 1347960280,
+    "varlen": {"digest": "185b0e45f1e5c5cc", "plan": "carry", "fetch_bytes": 4127717794, "write_bytes": 1347994840,
                "profile": "profiles/ssm_rows_kernel_varlen_bf16.md"},
-    "130m+conv4": {"digest": "6f7f3370409d5913", "plan": "mixed", "fetch_bytes": 320503286, "write_bytes": 101449730,
+    "130m+conv4": {"digest": "185b0e45f1e5c5cc", "plan": "mixed", "fetch_bytes": 320503002, "write_bytes": 101449735,
                    "profile": "profiles/ssm_mixed_kernel_conv4_130m_f32.md"},
 }
 
