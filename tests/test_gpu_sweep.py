@@ -80,7 +80,7 @@ def _bound(dtype):
     return 2e-2 if dtype == "bf16" else 1e-4
 
 
-FWD = _cases(7101, 36, with_plan=True)
+FWD = _cases(7101, 72, with_plan=True)
 
 
 @pytest.mark.parametrize("c", FWD, ids=[_id(c) for c in FWD])
@@ -97,7 +97,7 @@ def test_forward_sweep(c):
     assert ey <= _bound(c["dtype"]) and eh <= 1e-4, f"y {ey:.3e} last {eh:.3e}"
 
 
-STATES = _cases(7202, 16, with_plan=True)
+STATES = _cases(7202, 32, with_plan=True)
 
 
 @pytest.mark.parametrize("c", STATES, ids=[_id(c) for c in STATES])
@@ -128,7 +128,7 @@ def test_start_state_sweep(c):
     assert rel_err(_host(cs), want_cs) <= 1e-4
 
 
-BWD = _cases(7303, 16, with_plan=False)
+BWD = _cases(7303, 32, with_plan=False)
 IO_KEYS = ("du", "ddelta", "dz")
 
 
@@ -163,7 +163,7 @@ def test_backward_sweep(c):
 
 # ------------------------------------------------------- conv1d + SiLU in front
 
-CONV = _cases(7404, 16, with_plan=True)
+CONV = _cases(7404, 32, with_plan=True)
 
 
 @pytest.mark.parametrize("c", CONV, ids=[_id(c) for c in CONV])
@@ -190,7 +190,7 @@ def test_conv_forward_sweep(c):
     assert rel_err(_host(last), last_ref) <= 1e-4
 
 
-CONV_BWD = _cases(7505, 10, with_plan=False)
+CONV_BWD = _cases(7505, 40, with_plan=False)
 
 
 @pytest.mark.parametrize("c", CONV_BWD, ids=[_id(c) for c in CONV_BWD])
@@ -232,7 +232,7 @@ def test_conv_backward_sweep(c):
 
 # ------------------------------------------------------- decode steps
 
-STEP = _cases(7606, 12, with_plan=False)
+STEP = _cases(7606, 24, with_plan=False)
 
 
 @pytest.mark.parametrize("c", STEP, ids=[_id(c) for c in STEP])
@@ -292,7 +292,7 @@ def _proj_cases(seed, count):
     return out
 
 
-PROJ = _proj_cases(7707, 20)
+PROJ = _proj_cases(7707, 30)
 
 
 @pytest.mark.parametrize("c", PROJ, ids=[f"b{c['b']}k{c['k']}m{c['m']}L{c['L']}-{c['dtype']}" for c in PROJ])
@@ -320,7 +320,7 @@ def _affine_cases(seed, count):
              int(rng.integers(1 << 20))) for _ in range(count)]
 
 
-AFFINE = _affine_cases(7808, 16)
+AFFINE = _affine_cases(7808, 24)
 
 
 @pytest.mark.parametrize("rows,L,seed", AFFINE, ids=[f"r{r}L{l}" for r, l, _ in AFFINE])
